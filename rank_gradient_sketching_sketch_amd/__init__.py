@@ -1,0 +1,22 @@
+"""LoGRA sketch-accumulate + RowAdam-apply on MI355X (gfx950).
+
+The compute path is the C-ABI library ``liblogra.so`` (HIP kernels); the
+functions here are a thin ctypes binding over it. Importing the package does
+not load the library; the first call does, and fails loudly if it is not
+built.
+"""
+from __future__ import annotations
+
+__all__ = [
+    "logra_abi_version", "logra_status_string", "logra_sign_words",
+    "logra_sketch_workspace_bytes", "logra_sketch_accumulate",
+    "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
+    "LograError", "MatrixDesc", "library_path", "load_library",
+]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
