@@ -1,0 +1,243 @@
+"""Benchmark of the LoGRA sketch-accumulate + RowAdam-apply path on one GPU.
+
+One step = every microbatch of the step folded into the sketch
+(logra_sketch_project + logra_sketch_fold, i.e. logra_sketch_accumulate),
+pass 1 (logra_update_sqnorm) for every matrix, one device-to-host read of the
+sqnorms for the step controller, and pass 2 (logra_rowadam_apply) for every
+matrix. Inputs are synthetic and already resident in HBM; each microbatch of
+a step has its own buffers, so the inputs of one step (about 3 GB in the
+default workload) stream through the 256 MB last-level cache.
+
+Prints one JSON line. value = sketch-accumulate TFLOP/s (algorithmic
+2*T*r*(d+k) per microbatch call, over the HIP-event time of the sketch
+calls); the same line carries the RowAdam-apply GB/s, the roofline of the
+dominant kernel (the stage-2 fold) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen7b_up")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_gradient_sketching_sketch_amd import binding as B
+    from rank_gradient_sketching_sketch_amd import inputs
+
+    if not os.path.exists(B.LIB_PATH):
+        from rank_gradient_sketching_sketch_amd import build_lib
+        build_lib.build()
+    B.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = inputs.WORKLOADS[args.workload]
+    code = B.LOGRA_BF16 if wl.act_dtype == torch.bfloat16 else B.LOGRA_F32
+    T, r, nmb = wl.tokens, wl.r, wl.microbatches
+
+    # ---- resident state and inputs -------------------------------------
+    mats = []
+    for spec in wl.matrices:
+        mats.append({
+            "spec": spec,
+            "S": torch.empty(spec.d, r, dtype=torch.float32, device=dev),
+            "v": inputs.second_moment(wl, spec, device=dev),
+            "W": inputs.weights(wl, spec, device=dev),
+            "rowsq": torch.empty(spec.d, dtype=torch.float32, device=dev),
+            "sq": torch.empty(1, dtype=torch.float32, device=dev),
+        })
+    ws_bytes = max(B.logra_sketch_workspace_bytes(B.MatrixDesc(s.d, s.k, r), T, code)
+                   for s in wl.matrices)
+    ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+    sq_ws_bytes = max(B.logra_sqnorm_workspace_bytes(B.MatrixDesc(s.d, s.k, r), code)
+                      for s in wl.matrices)
+    sq_ws = torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev)
+    # one set of microbatch buffers per (input shape, microbatch)
+    xbuf, ybuf = {}, {}
+    for spec in wl.matrices:
+        for mb in range(nmb):
+            xkey = (inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)
+            if xkey not in xbuf:
+                xbuf[xkey] = inputs.activations(wl, spec, 0, mb, device=dev)
+            ykey = (spec.matrix_id, mb)
+            ybuf[ykey] = inputs.output_grads(wl, spec, 0, mb, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    sketch_flop_per_step = sum(2.0 * T * r * (s.d + s.k) for s in wl.matrices) * nmb
+    fold_bytes_per_step = 0.0
+    for s in wl.matrices:
+        for mb in range(nmb):
+            fold_bytes_per_step += 2.0 * T * s.d + 2.0 * T * r + 4.0 * s.d * r * (2 if mb > 0 else 1)
+    wbytes = 2 if wl.w_dtype == torch.bfloat16 else 4
+    apply_bytes_per_step = sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * r + 8.0 * s.d + 8.0 * s.d
+                               for s in wl.matrices)
+
+    ev_log = []   # (kind, start_event, end_event)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    skipped = [0]
+
+    def one_step(step, timed):
+        for m in mats:
+            spec = m["spec"]
+            desc = B.MatrixDesc(spec.d, spec.k, r, seed=0, step=step, matrix_id=spec.matrix_id)
+            m["desc"] = desc
+            for mb in range(nmb):
+                X = xbuf[(inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)]
+                dY = ybuf[(spec.matrix_id, mb)]
+                e0 = ev() if timed else None
+                B.logra_sketch_project(desc, X, ws, stream)
+                e1 = ev() if timed else None
+                B.logra_sketch_fold(desc, dY, m["S"], mb > 0, ws, stream)
+                if timed:
+                    e2 = ev()
+                    ev_log.append(("project", e0, e1))
+                    ev_log.append(("fold", e1, e2))
+        e0 = ev() if timed else None
+        for m in mats:
+            B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["rowsq"],
+                                  m["sq"], sq_ws, stream)
+        if timed:
+            ev_log.append(("sqnorm", e0, ev()))
+        # step controller stand-in: read every sqnorm, skip non-finite ones,
+        # use the drawn scale (the controller's formula is not part of this path)
+        sqs = torch.cat([m["sq"] for m in mats]).cpu().tolist()
+        e0 = ev() if timed else None
+        for m, sq in zip(mats, sqs):
+            if not math.isfinite(sq):
+                skipped[0] += 1
+                continue
+            scale = inputs.step_scale(wl, m["spec"], step)
+            B.logra_rowadam_apply(m["desc"], code, m["S"], m["v"], m["rowsq"], m["W"], wl.lr, scale,
+                                  wl.beta2, wl.eps, stream)
+        if timed:
+            ev_log.append(("apply", e0, ev()))
+
+    for s in range(args.warmup):
+        one_step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step(args.warmup + s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    tot = {"project": 0.0, "fold": 0.0, "sqnorm": 0.0, "apply": 0.0}
+    cnt = {k: 0 for k in tot}
+    for kind, a, b in ev_log:
+        tot[kind] += a.elapsed_time(b)
+        cnt[kind] += 1
+    K = args.steps
+    sketch_ms = (tot["project"] + tot["fold"]) / K
+    apply_ms = (tot["sqnorm"] + tot["apply"]) / K
+    sketch_tflops = sketch_flop_per_step / (sketch_ms * 1e-3) / 1e12
+    apply_gbps = apply_bytes_per_step / (apply_ms * 1e-3) / 1e9
+    fold_avg_ms = tot["fold"] / max(1, cnt["fold"])
+    fold_bytes_avg = fold_bytes_per_step / (nmb * len(mats))
+    fold_gbps = fold_bytes_avg / (fold_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(sketch_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if code == B.LOGRA_BF16 else "f32",
+        "data": "synthetic (seeded Gaussian inputs of the workload's shapes; no datasets or weights)",
+        "config": {"workload": wl.name, "description": wl.description, "r": r,
+                   "microbatches": nmb, "tokens": T, "matrices": len(mats),
+                   "shapes": sorted({(s.d, s.k) for s in wl.matrices})},
+        "sketch": {"tflops": round(sketch_tflops, 2),
+                   "frac_mfma_peak": round(sketch_tflops / PEAK_BF16_TFLOPS, 4),
+                   "ms_per_step": round(sketch_ms, 4),
+                   "project_ms_per_call": round(tot["project"] / max(1, cnt["project"]), 5),
+                   "fold_ms_per_call": round(fold_avg_ms, 5)},
+        "apply": {"GBps": round(apply_gbps, 1), "frac_hbm_peak": round(apply_gbps / PEAK_HBM_GBPS, 4),
+                  "ms_per_step": round(apply_ms, 4),
+                  "sqnorm_ms": round(tot["sqnorm"] / K, 5), "rowadam_ms": round(tot["apply"] / K, 5),
+                  "skipped_nonfinite": skipped[0]},
+        "roofline": {"kernel": "stage2_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
+                     "achieved": round(fold_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(fold_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": round(fold_bytes_avg)},
+        "state_bytes": {"sketch_plus_v": sum(4 * s.d * r + 4 * s.d for s in wl.matrices),
+                        "dense_grad_fp32": sum(4 * s.d * s.k for s in wl.matrices)},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands, on one microbatch of the workload's first
+    matrix, all rows: P = X A^T then S = dY^T P (the sketch-accumulate unit)."""
+    import oracle
+    import torch
+    from rank_gradient_sketching_sketch_amd import inputs
+    spec = wl.matrices[0]
+    X = inputs.activations(wl, spec, 0, 0).double().numpy()
+    dY = inputs.output_grads(wl, spec, 0, 0).double().numpy()
+    A = oracle.sign_matrix(0, 0, spec.matrix_id, wl.r, spec.k)
+    t0 = time.perf_counter()
+    P = oracle.project(X, A)
+    oracle.sketch_rows(dY, P)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * wl.tokens * wl.r * (spec.d + spec.k)
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu": cpu_model(),
+            "sample": "one microbatch (%d tokens) of the %s %dx%d projection, all rows, fp64"
+                      % (wl.tokens, spec.name, spec.d, spec.k)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * logra.h -- C ABI of liblogra.so: LoGRA low-rank gradient sketching and
+ * RowAdam apply on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages on LoGRA: "NVIDIA's LoGRA fits RL post-training of a 27B
+ * model onto a single eight-GPU node", sections "What happened" and "Why it
+ * matters"; "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
+ * Sketches", paragraphs "Gradient sketches." and "Step control."):
+ *
+ *   For a selected linear projection W (d x k, row-major [out, in]) every
+ *   microbatch with activations X (T x k) and output gradients dY (T x d)
+ *   adds to a d x r sketch
+ *         S += dY^T (X A^T),
+ *   so the d x k gradient G = dY^T X is never formed. A = Sigma / sqrt(r) is
+ *   an r x k random-sign matrix, redrawn each optimizer step and fixed
+ *   within it; it is never stored: every kernel regenerates the signs it
+ *   needs from a counter hash of (seed, step, matrix_id). At update time the
+ *   estimate Ghat = S A is rebuilt tile by tile, twice:
+ *     pass 1 (logra_update_sqnorm): rowsq_i = sum_j Ghat_ij^2 and the
+ *        controller's reduction sqnorm = sum_ij (Ghat_ij / (sqrt(v'_i)+eps))^2
+ *        with v'_i = beta2 v_i + (1 - beta2) rowsq_i / k;
+ *     pass 2 (logra_rowadam_apply): v <- v', W_ij -= lr*scale*Ghat_ij /
+ *        (sqrt(v'_i) + eps). RowAdam keeps one second moment per row and no
+ *        first moment.
+ *   A host-side step controller reads sqnorm between the two passes and
+ *   picks scale; the controller is not part of this library.
+ *
+ * Sign hash (fixed so that any implementation reproduces A bit for bit):
+ *   mix(z)   : SplitMix64 finaliser, z ^= z>>30; z *= 0xBF58476D1CE4E5B9;
+ *              z ^= z>>27; z *= 0x94D049BB133111EB; z ^= z>>31 (mod 2^64)
+ *   h(x)     = mix(x + 0x9E3779B97F4A7C15)
+ *   key      = h(h(h(seed) ^ step) ^ matrix_id)
+ *   word(l,b)= mix(key + (((l << 32) | b) + 1) * 0x9E3779B97F4A7C15)
+ *   Sigma[l][j] = -1 if bit (j mod 64) of word(l, j/64) is 1, else +1.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *     allocates nothing, keeps no mutable global state and is reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is
+ *     enqueued asynchronously on it; results are visible after the caller
+ *     synchronises the stream.
+ *   - Arguments are validated before anything is enqueued. On any error
+ *     nothing is launched and no output is touched.
+ *   - Output buffers must not alias each other or the inputs.
+ *   - Non-finite inputs are not checked; they propagate into the outputs.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no atomics in any reduction, fixed summation orders).
+ *   - Matrices are row-major with a leading dimension (row stride, in
+ *     elements) >= the number of columns.
+ */
+#ifndef LOGRA_H_
+#define LOGRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOGRA_ABI_VERSION 1
+
+typedef enum logra_status {
+    LOGRA_OK = 0,
+    LOGRA_ERR_INVALID_ARGUMENT = 1, /* null/negative/misaligned/out-of-range */
+    LOGRA_ERR_UNSUPPORTED = 2,      /* valid, but outside what the kernels do */
+    LOGRA_ERR_WORKSPACE = 3,        /* workspace missing or too small        */
+    LOGRA_ERR_HIP = 4               /* a HIP launch reported an error        */
+} logra_status;
+
+typedef enum logra_dtype {
+    LOGRA_F32 = 0,
+    LOGRA_BF16 = 1
+} logra_dtype;
+
+/* One sketched matrix in one optimizer step. d = rows of W (output
+ * features), k = columns (input features), r = sketch rank. (seed, step,
+ * matrix_id) select the sign matrix A of this step. */
+typedef struct logra_matrix {
+    int64_t d;
+    int64_t k;
+    int64_t r;
+    uint64_t seed;
+    uint64_t step;
+    uint64_t matrix_id;
+} logra_matrix;
+
+/* ABI version of the loaded library (LOGRA_ABI_VERSION). */
+int logra_abi_version(void);
+
+/* Static string naming a status code. Never NULL. */
+const char *logra_status_string(int status);
+
+/*
+ * logra_sign_words -- write the packed sign words of this step's A.
+ * Defines: the counter hash above (A is random-sign, redrawn per step and
+ * fixed across the step's microbatches: "LoGRA: Scaling LLM Reinforcement
+ * Learning...", paragraph "Gradient sketches.").
+ * words: device, r x ceil(k/64) uint64, row-major; words[l*nb + b] =
+ *        word(l, b). Bits beyond column k-1 in the last word are hash bits
+ *        that no kernel uses.
+ * Errors: INVALID_ARGUMENT for m == NULL, words == NULL, d/k/r <= 0.
+ */
+logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stream);
+
+/*
+ * logra_sketch_workspace_bytes -- device workspace that
+ * logra_sketch_accumulate needs for these sizes (0 when T == 0). Returns 0
+ * and sets nothing for invalid arguments (m NULL, sizes <= 0, T < 0, bad
+ * dtype). The workspace holds the projected microbatch X A^T and its split
+ * partial sums; it is scratch, free to reuse once the call's work has run.
+ */
+size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dtype);
+
+/*
+ * logra_sketch_accumulate -- fold one microbatch into the sketch:
+ *        S  = dY^T (X A^T)        (accumulate == 0)
+ *        S += dY^T (X A^T)        (accumulate != 0)
+ * Defines: S = G A^T with G = dY^T X the d x k weight gradient, accumulated
+ * during backpropagation as microbatches arrive ("NVIDIA's LoGRA fits RL
+ * post-training...", section "Why it matters"; "LoGRA: Scaling LLM
+ * Reinforcement Learning...", paragraph "Gradient sketches.").
+ * Arguments:
+ *   T        tokens in this microbatch (>= 0). T == 0 leaves S unchanged
+ *            (accumulate != 0) or sets it to zero (accumulate == 0).
+ *   act_dtype LOGRA_BF16: X, dY are bf16; products run on bf16 MFMA with fp32
+ *            accumulation, and X A^T is rounded to bf16 (nearest even)
+ *            before the second product. LOGRA_F32: fp32 throughout, no
+ *            reduced-precision shortcuts.
+ *   X        T x k, row stride ldx >= k.
+ *   dY       T x d, row stride lddy >= d.
+ *   S        d x r fp32, row-major, stride r; in/out.
+ *   ws       device workspace of ws_bytes >= logra_sketch_workspace_bytes().
+ * Requirements of the bf16 path: r in {32, 64, 128, 256}; d, k, ldx, lddy
+ *   multiples of 8; X, dY 16-byte aligned. The fp32 path takes any r in
+ *   [1, 1024] and any d, k >= 1. S and ws must be 16-byte aligned.
+ * Errors: INVALID_ARGUMENT (null pointer when T > 0, sizes <= 0, T < 0,
+ *   ld < cols, misalignment), UNSUPPORTED (r or shape outside the above,
+ *   unknown dtype), WORKSPACE (ws NULL or ws_bytes too small), HIP.
+ */
+logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_dtype,
+                                     const void *X, int64_t ldx,
+                                     const void *dY, int64_t lddy,
+                                     float *S, int accumulate,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * logra_sketch_project / logra_sketch_fold -- the two halves of
+ * logra_sketch_accumulate, for callers that schedule them separately (for
+ * example to time them, or to overlap the projection of the next microbatch
+ * with the fold of this one on another stream, each with its own workspace).
+ * Calling project then fold with the same (m, T, act_dtype) and workspace is
+ * exactly logra_sketch_accumulate: same kernels, same results.
+ *   project: workspace <- X A^T (bf16 path: rounded to bf16, nearest even;
+ *            fp32 path: fp32). Same arguments and errors as accumulate.
+ *   fold:    S (+)= dY^T (X A^T) reading the projection from the workspace.
+ *            The workspace must hold a projection of this (m, T, act_dtype)
+ *            made by logra_sketch_project; fold does not check that it does.
+ * Sources: as logra_sketch_accumulate (S = G A^T factored as dY^T (X A^T)).
+ */
+logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtype,
+                                  const void *X, int64_t ldx,
+                                  void *ws, size_t ws_bytes, void *stream);
+logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
+                               const void *dY, int64_t lddy,
+                               float *S, int accumulate,
+                               const void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs
+ * (per-block partial sums of the sqnorm reduction). 0 for invalid m.
+ */
+size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype);
+
+/*
+ * logra_update_sqnorm -- apply pass 1. Rebuilds Ghat = S A tile by tile and
+ * reduces, without changing any state:
+ *   rowsq[i] = sum_j Ghat_ij^2                                  (d floats)
+ *   sqnorm[0] = sum_i rowsq_i * u_i^2, u_i = 1/(sqrt(v'_i) + eps),
+ *               v'_i = beta2 * v[i] + (1 - beta2) * rowsq_i / k
+ * sum_i rowsq_i u_i^2 equals sum_ij (Ghat_ij u_i)^2 because u is constant
+ * along a row. sqnorm is the per-matrix quantity a predicted-KL step
+ * controller reads before the update ("LoGRA: Scaling LLM Reinforcement
+ * Learning...", paragraph "Step control."; the KL from the sketch alone:
+ * "NVIDIA's LoGRA fits RL post-training...", section "Why it matters"). The
+ * row second moment is RowAdam's ("What happened" on the same page).
+ * Arguments:
+ *   compute_dtype LOGRA_BF16: S is rounded to bf16 (nearest even) as the
+ *            MFMA operand, fp32 accumulation. LOGRA_F32: fp32 arithmetic.
+ *   S        d x r fp32 (stride r). v: d fp32 (current second moment).
+ *   rowsq    d fp32, out. sqnorm: 1 fp32 on the device, out.
+ *   ws       device workspace of ws_bytes >= logra_sqnorm_workspace_bytes().
+ * Requirements: bf16 path r in {32, 64, 128, 256} and k multiple of 8; fp32
+ *   path r in [1, 1024]. Pointers 16-byte aligned.
+ * Errors: INVALID_ARGUMENT (nulls, sizes, beta2 outside [0,1], eps < 0,
+ *   misalignment), UNSUPPORTED, WORKSPACE, HIP.
+ */
+logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype,
+                                 const float *S, const float *v,
+                                 float beta2, float eps,
+                                 float *rowsq, float *sqnorm,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * logra_rowadam_apply -- apply pass 2. Commits v[i] <- v'_i and updates
+ *   W_ij <- W_ij - lr * scale * Ghat_ij / (sqrt(v'_i) + eps)
+ * with Ghat = S A rebuilt tile by tile and v'_i from the rowsq that
+ * logra_update_sqnorm produced for the same S, v, beta2 (RowAdam, "NVIDIA's
+ * LoGRA fits RL post-training...", sections "What happened" and "Why it
+ * matters"; the update is rebuilt from the two small factors at the moment
+ * it is applied, same page). scale is the step controller's factor.
+ * Arguments:
+ *   compute_dtype as in logra_update_sqnorm.
+ *   S        d x r fp32. v: d fp32, in/out. rowsq: d fp32, in.
+ *   W        d x k, row stride ldw >= k, dtype w_dtype (fp32 math, stored
+ *            back at its dtype; bf16 by round-to-nearest-even), in/out.
+ * Requirements: as logra_update_sqnorm; bf16 W or bf16 compute also need
+ *   ldw multiple of 8 and W 16-byte aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP, as above.
+ */
+logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype,
+                                 const float *S, float *v, const float *rowsq,
+                                 void *W, int w_dtype, int64_t ldw,
+                                 float lr, float scale, float beta2, float eps,
+                                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGRA_H_ */

@@ -43,6 +43,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     u64, i64, dbl = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double
     P = ctypes.c_void_p
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
     lib.oracle_mix64.restype = u64
     lib.oracle_mix64.argtypes = [u64]
     lib.oracle_splitmix64_output.restype = u64
@@ -74,6 +76,11 @@ def _f64(a) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().oracle_num_threads())
 
 
 # ------------------------------------------------------------------ hash ---

@@ -47,6 +47,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ---------------------------------------------------------------- hash --- */
 
 #define SM64_GAMMA 0x9E3779B97F4A7C15ULL

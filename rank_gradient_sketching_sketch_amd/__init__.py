@@ -10,6 +10,7 @@ from __future__ import annotations
 __all__ = [
     "logra_abi_version", "logra_status_string", "logra_sign_words",
     "logra_sketch_workspace_bytes", "logra_sketch_accumulate",
+    "logra_sketch_project", "logra_sketch_fold",
     "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
     "LograError", "MatrixDesc", "library_path", "load_library",
 ]

@@ -1,0 +1,189 @@
+"""ctypes binding of liblogra.so (declared in include/logra.h).
+
+Argument marshalling only: tensors become device pointers, leading
+dimensions and dtypes are read from the tensors, the stream defaults to
+torch's current stream. Every step of the computation runs in the HIP
+kernels behind the C ABI; there is no fallback of any kind, and a missing or
+unloadable library raises LograError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblogra.so")
+
+LOGRA_F32 = 0
+LOGRA_BF16 = 1
+_STATUS = {0: "LOGRA_OK", 1: "LOGRA_ERR_INVALID_ARGUMENT", 2: "LOGRA_ERR_UNSUPPORTED",
+           3: "LOGRA_ERR_WORKSPACE", 4: "LOGRA_ERR_HIP"}
+
+
+class LograError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, _STATUS.get(status, str(status))))
+
+
+class MatrixDesc(ctypes.Structure):
+    """logra_matrix: d x k projection, rank r, and the (seed, step, id) of A."""
+    _fields_ = [("d", ctypes.c_int64), ("k", ctypes.c_int64), ("r", ctypes.c_int64),
+                ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64),
+                ("matrix_id", ctypes.c_uint64)]
+
+    def __init__(self, d, k, r, seed=0, step=0, matrix_id=0):
+        super().__init__(int(d), int(k), int(r), int(seed), int(step), int(matrix_id))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LograError(-1, "load liblogra.so (not built: run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, u64, f32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                 ctypes.c_float, ctypes.c_int, ctypes.c_size_t)
+    D = ctypes.POINTER(MatrixDesc)
+    lib.logra_abi_version.restype = i32
+    lib.logra_abi_version.argtypes = []
+    lib.logra_status_string.restype = ctypes.c_char_p
+    lib.logra_status_string.argtypes = [i32]
+    lib.logra_sign_words.restype = i32
+    lib.logra_sign_words.argtypes = [D, P, P]
+    lib.logra_sketch_workspace_bytes.restype = sz
+    lib.logra_sketch_workspace_bytes.argtypes = [D, i64, i32]
+    lib.logra_sketch_accumulate.restype = i32
+    lib.logra_sketch_accumulate.argtypes = [D, i64, i32, P, i64, P, i64, P, i32, P, sz, P]
+    lib.logra_sketch_project.restype = i32
+    lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, P]
+    lib.logra_sketch_fold.restype = i32
+    lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, P]
+    lib.logra_sqnorm_workspace_bytes.restype = sz
+    lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
+    lib.logra_update_sqnorm.restype = i32
+    lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, sz, P]
+    lib.logra_rowadam_apply.restype = i32
+    lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, P, i32, i64, f32, f32, f32, f32, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LograError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LOGRA_BF16
+    if t.dtype == torch.float32:
+        return LOGRA_F32
+    raise LograError(2, "dtype %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise LograError(1, "2-D tensor with unit column stride expected")
+    return t.stride(0)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def logra_abi_version() -> int:
+    return int(load_library().logra_abi_version())
+
+
+def logra_status_string(status: int) -> str:
+    return load_library().logra_status_string(int(status)).decode()
+
+
+def logra_sign_words(m: MatrixDesc, words: torch.Tensor, stream=None) -> None:
+    """words: int64/uint64 device tensor of r * ceil(k/64) elements."""
+    _check(load_library().logra_sign_words(ctypes.byref(m), _ptr(words), _stream(stream)),
+           "logra_sign_words")
+
+
+def logra_sketch_workspace_bytes(m: MatrixDesc, T: int, act_dtype: int) -> int:
+    return int(load_library().logra_sketch_workspace_bytes(ctypes.byref(m), int(T), int(act_dtype)))
+
+
+def logra_sketch_accumulate(m: MatrixDesc, X: torch.Tensor, dY: torch.Tensor, S: torch.Tensor,
+                            accumulate: bool, ws: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """S (+)= dY^T (X A^T) for one microbatch; X is T x k, dY is T x d."""
+    T = X.shape[0]
+    code = _dtype_code(X)
+    ws, ws_bytes = _sketch_ws(m, T, code, S.device, ws)
+    _check(load_library().logra_sketch_accumulate(
+        ctypes.byref(m), T, code, _ptr(X), _ld(X), _ptr(dY), _ld(dY), _ptr(S),
+        1 if accumulate else 0, _ptr(ws), ws_bytes, _stream(stream)), "logra_sketch_accumulate")
+
+
+def _sketch_ws(m, T, code, device, ws):
+    if ws is None:
+        nbytes = logra_sketch_workspace_bytes(m, T, code)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def logra_sketch_project(m: MatrixDesc, X: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """workspace <- X A^T for one microbatch (first half of sketch_accumulate)."""
+    ws, nb = _sketch_ws(m, X.shape[0], _dtype_code(X), X.device, ws)
+    _check(load_library().logra_sketch_project(
+        ctypes.byref(m), X.shape[0], _dtype_code(X), _ptr(X), _ld(X), _ptr(ws), nb,
+        _stream(stream)), "logra_sketch_project")
+
+
+def logra_sketch_fold(m: MatrixDesc, dY: torch.Tensor, S: torch.Tensor, accumulate: bool,
+                      ws: torch.Tensor, stream=None) -> None:
+    """S (+)= dY^T (X A^T) with the projection left in ws by logra_sketch_project."""
+    ws, nb = _sketch_ws(m, dY.shape[0], _dtype_code(dY), dY.device, ws)
+    _check(load_library().logra_sketch_fold(
+        ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(S),
+        1 if accumulate else 0, _ptr(ws), nb, _stream(stream)), "logra_sketch_fold")
+
+
+def logra_sqnorm_workspace_bytes(m: MatrixDesc, compute_dtype: int) -> int:
+    return int(load_library().logra_sqnorm_workspace_bytes(ctypes.byref(m), int(compute_dtype)))
+
+
+def logra_update_sqnorm(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
+                        beta2: float, eps: float, rowsq: torch.Tensor, sqnorm: torch.Tensor,
+                        ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    if ws is None:
+        nbytes = logra_sqnorm_workspace_bytes(m, compute_dtype)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=S.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(load_library().logra_update_sqnorm(
+        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
+        _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws_bytes, _stream(stream)), "logra_update_sqnorm")
+
+
+def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
+                        rowsq: torch.Tensor, W: torch.Tensor, lr: float, scale: float,
+                        beta2: float, eps: float, stream=None) -> None:
+    _check(load_library().logra_rowadam_apply(
+        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), _ptr(rowsq), _ptr(W),
+        _dtype_code(W), _ld(W), float(lr), float(scale), float(beta2), float(eps),
+        _stream(stream)), "logra_rowadam_apply")

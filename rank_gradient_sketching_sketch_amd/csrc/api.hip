@@ -1,0 +1,236 @@
+// C ABI of liblogra.so: argument validation, per-step key derivation, work
+// planning and kernel dispatch. Declarations and the contract of every entry
+// point are in include/logra.h. Nothing here allocates memory or keeps state:
+// every buffer, workspace included, comes from the caller.
+#include <math.h>
+
+#include "../../include/logra.h"
+#include "launch.hpp"
+#include "signs.hpp"
+
+using namespace logra;
+
+namespace {
+
+// key = h(h(h(seed) ^ step) ^ matrix_id), h(x) = first SplitMix64 output of x.
+uint64_t stream_key(uint64_t seed, uint64_t step, uint64_t matrix_id) {
+    auto h = [](uint64_t x) { return splitmix_finalize(x + kGolden); };
+    return h(h(h(seed) ^ step) ^ matrix_id);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bf16_rank_ok(int64_t r) { return r == 32 || r == 64 || r == 128 || r == 256; }
+
+bool matrix_ok(const logra_matrix *m) {
+    return m && m->d > 0 && m->k > 0 && m->r > 0 && m->d <= (1ll << 30) && m->k <= (1ll << 30);
+}
+
+logra_status from_hip(hipError_t e) { return e == hipSuccess ? LOGRA_OK : LOGRA_ERR_HIP; }
+
+float inv_sqrt_rank(int64_t r) { return 1.0f / sqrtf(static_cast<float>(r)); }
+
+size_t sqnorm_partials(const logra_matrix *m, int compute_dtype) {
+    const int n = compute_dtype == LOGRA_BF16 ? apply_blocks_bf16(m->d) : apply_blocks_f32(m->d);
+    return static_cast<size_t>(n) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int logra_abi_version(void) { return LOGRA_ABI_VERSION; }
+
+const char *logra_status_string(int status) {
+    switch (status) {
+    case LOGRA_OK: return "LOGRA_OK";
+    case LOGRA_ERR_INVALID_ARGUMENT: return "LOGRA_ERR_INVALID_ARGUMENT";
+    case LOGRA_ERR_UNSUPPORTED: return "LOGRA_ERR_UNSUPPORTED";
+    case LOGRA_ERR_WORKSPACE: return "LOGRA_ERR_WORKSPACE";
+    case LOGRA_ERR_HIP: return "LOGRA_ERR_HIP";
+    default: return "LOGRA_UNKNOWN_STATUS";
+    }
+}
+
+logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stream) {
+    if (!matrix_ok(m) || !words) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (m->r > (1ll << 20)) return LOGRA_ERR_UNSUPPORTED;
+    const uint64_t key = stream_key(m->seed, m->step, m->matrix_id);
+    return from_hip(launch_sign_words(key, static_cast<int>(m->r), static_cast<int>(m->k), words,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dtype) {
+    if (!matrix_ok(m) || T < 0) return 0;
+    if (T == 0) return 0;
+    if (act_dtype == LOGRA_BF16) {
+        if (!bf16_rank_ok(m->r)) return 0;
+        const Stage1Plan p = plan_stage1_bf16(T, m->k, static_cast<int>(m->r));
+        return p.part_bytes + p.p_bytes;
+    }
+    if (act_dtype == LOGRA_F32) return workspace_sketch_f32(T, m->r);
+    return 0;
+}
+
+static logra_status check_sketch(const logra_matrix *m, int64_t T, int act_dtype) {
+    if (!matrix_ok(m) || T < 0) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype != LOGRA_F32 && act_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
+    if (T > (1ll << 30)) return LOGRA_ERR_UNSUPPORTED;
+    if (act_dtype == LOGRA_BF16) {
+        if (!bf16_rank_ok(m->r) || m->d % 8 || m->k % 8) return LOGRA_ERR_UNSUPPORTED;
+    } else if (m->r > 1024) {
+        return LOGRA_ERR_UNSUPPORTED;
+    }
+    return LOGRA_OK;
+}
+
+static logra_status check_project(const logra_matrix *m, int64_t T, int act_dtype, const void *X,
+                                  int64_t ldx, const void *ws, size_t ws_bytes) {
+    if (T == 0) return LOGRA_OK;
+    if (!X || ldx < m->k) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype == LOGRA_BF16 && (ldx % 8 || !aligned16(X))) return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = logra_sketch_workspace_bytes(m, T, act_dtype);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    return LOGRA_OK;
+}
+
+static logra_status check_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
+                               int64_t lddy, const float *S, const void *ws, size_t ws_bytes) {
+    if (!S || !aligned16(S)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return LOGRA_OK;
+    if (!dY || lddy < m->d) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype == LOGRA_BF16 && (lddy % 8 || !aligned16(dY))) return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = logra_sketch_workspace_bytes(m, T, act_dtype);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    return LOGRA_OK;
+}
+
+static hipError_t do_project(const logra_matrix *m, int64_t T, int act_dtype, const void *X,
+                             int64_t ldx, void *ws, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    const uint64_t key = stream_key(m->seed, m->step, m->matrix_id);
+    const float c = inv_sqrt_rank(m->r);
+    const int r = static_cast<int>(m->r);
+    if (act_dtype == LOGRA_BF16)
+        return launch_project_bf16(r, T, m->k, key, c, static_cast<const uint16_t *>(X), ldx, ws, st);
+    return launch_project_f32(r, T, m->k, key, c, static_cast<const float *>(X), ldx, ws, st);
+}
+
+static hipError_t do_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
+                          int64_t lddy, float *S, int accumulate, const void *ws, hipStream_t st) {
+    if (T == 0) return accumulate ? hipSuccess : launch_fill_zero(S, m->d * m->r, st);
+    const int r = static_cast<int>(m->r);
+    if (act_dtype == LOGRA_BF16)
+        return launch_fold_bf16(r, T, m->d, m->k, static_cast<const uint16_t *>(dY), lddy, S,
+                                accumulate ? 1 : 0, ws, st);
+    return launch_fold_f32(r, T, m->d, static_cast<const float *>(dY), lddy, S, accumulate ? 1 : 0,
+                           ws, st);
+}
+
+logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtype, const void *X,
+                                  int64_t ldx, void *ws, size_t ws_bytes, void *stream) {
+    logra_status e = check_sketch(m, T, act_dtype);
+    if (e == LOGRA_OK) e = check_project(m, T, act_dtype, X, ldx, ws, ws_bytes);
+    if (e != LOGRA_OK) return e;
+    return from_hip(do_project(m, T, act_dtype, X, ldx, ws, static_cast<hipStream_t>(stream)));
+}
+
+logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
+                               int64_t lddy, float *S, int accumulate, const void *ws,
+                               size_t ws_bytes, void *stream) {
+    logra_status e = check_sketch(m, T, act_dtype);
+    if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
+    if (e != LOGRA_OK) return e;
+    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws,
+                            static_cast<hipStream_t>(stream)));
+}
+
+logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_dtype,
+                                     const void *X, int64_t ldx, const void *dY, int64_t lddy,
+                                     float *S, int accumulate, void *ws, size_t ws_bytes,
+                                     void *stream) {
+    logra_status e = check_sketch(m, T, act_dtype);
+    if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
+    if (e == LOGRA_OK) e = check_project(m, T, act_dtype, X, ldx, ws, ws_bytes);
+    if (e != LOGRA_OK) return e;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t h = do_project(m, T, act_dtype, X, ldx, ws, st);
+    if (h != hipSuccess) return LOGRA_ERR_HIP;
+    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, st));
+}
+
+size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype) {
+    if (!matrix_ok(m)) return 0;
+    if (compute_dtype != LOGRA_F32 && compute_dtype != LOGRA_BF16) return 0;
+    return sqnorm_partials(m, compute_dtype);
+}
+
+static logra_status check_apply_common(const logra_matrix *m, int compute_dtype, const float *S,
+                                       float beta2, float eps) {
+    if (!matrix_ok(m) || !S) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!(beta2 >= 0.f && beta2 <= 1.f) || !(eps >= 0.f)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (compute_dtype == LOGRA_BF16) {
+        if (!bf16_rank_ok(m->r) || m->k % 8) return LOGRA_ERR_UNSUPPORTED;
+    } else if (compute_dtype == LOGRA_F32) {
+        if (m->r > 1024) return LOGRA_ERR_UNSUPPORTED;
+    } else {
+        return LOGRA_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(S)) return LOGRA_ERR_INVALID_ARGUMENT;
+    return LOGRA_OK;
+}
+
+static ApplyArgs base_args(const logra_matrix *m, const float *S, float beta2, float eps) {
+    ApplyArgs a;
+    a.R = static_cast<int>(m->r);
+    a.D = m->d;
+    a.K = m->k;
+    a.key = stream_key(m->seed, m->step, m->matrix_id);
+    a.c = inv_sqrt_rank(m->r);
+    a.S = S;
+    a.beta2 = beta2;
+    a.eps = eps;
+    return a;
+}
+
+logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const float *S,
+                                 const float *v, float beta2, float eps, float *rowsq,
+                                 float *sqnorm, void *ws, size_t ws_bytes, void *stream) {
+    logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
+    if (stt != LOGRA_OK) return stt;
+    if (!v || !rowsq || !sqnorm) return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = sqnorm_partials(m, compute_dtype);
+    if (!ws || ws_bytes < need) return LOGRA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ApplyArgs a = base_args(m, S, beta2, eps);
+    a.v_in = v;
+    a.rowsq_out = rowsq;
+    a.partials = static_cast<float *>(ws);
+    hipError_t e = compute_dtype == LOGRA_BF16 ? launch_apply_bf16(0, a, st) : launch_apply_f32(0, a, st);
+    if (e != hipSuccess) return LOGRA_ERR_HIP;
+    const int nparts = static_cast<int>(need / sizeof(float));
+    return from_hip(launch_sqnorm_final(a.partials, nparts, sqnorm, st));
+}
+
+logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const float *S,
+                                 float *v, const float *rowsq, void *W, int w_dtype, int64_t ldw,
+                                 float lr, float scale, float beta2, float eps, void *stream) {
+    logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
+    if (stt != LOGRA_OK) return stt;
+    if (!v || !rowsq || !W) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (w_dtype != LOGRA_F32 && w_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
+    if (ldw < m->k) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (compute_dtype == LOGRA_BF16 && (ldw % 8 || !aligned16(W))) return LOGRA_ERR_INVALID_ARGUMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ApplyArgs a = base_args(m, S, beta2, eps);
+    a.v = v;
+    a.rowsq_in = rowsq;
+    a.lr_scale = lr * scale;
+    a.W = W;
+    a.w_bf16 = w_dtype == LOGRA_BF16 ? 1 : 0;
+    a.ldw = ldw;
+    return from_hip(compute_dtype == LOGRA_BF16 ? launch_apply_bf16(1, a, st)
+                                                : launch_apply_f32(1, a, st));
+}
+
+}  // extern "C"

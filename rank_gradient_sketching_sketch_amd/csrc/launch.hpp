@@ -1,0 +1,63 @@
+// Internal launchers of liblogra.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace logra {
+
+// Work split of the first sketch product P = X A^T (bf16 path): row tiles of
+// tile_m tokens times `ks` chunks of k, each chunk kchunk columns (a multiple
+// of 64). Partial sums live in the workspace, followed by P in bf16.
+struct Stage1Plan {
+    int tile_m = 0;
+    int n_mtiles = 0;
+    int ks = 0;
+    int kchunk = 0;
+    int64_t t_pad = 0;        // n_mtiles * tile_m
+    size_t part_bytes = 0;    // ks * t_pad * r * 4
+    size_t p_bytes = 0;       // t_pad * r * 2
+};
+
+Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R);
+size_t workspace_sketch_f32(int64_t T, int64_t R);
+int apply_blocks_bf16(int64_t D);
+int apply_blocks_f32(int64_t D);
+
+hipError_t launch_sign_words(uint64_t key, int R, int K, uint64_t *words, hipStream_t st);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t st);
+
+// stage 1: P = c X Sigma^T into the workspace; stage 2: S (+)= dY^T P from it.
+hipError_t launch_project_bf16(int R, int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
+                               int64_t ldx, void *ws, hipStream_t st);
+hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
+                            float *S, int accumulate, const void *ws, hipStream_t st);
+hipError_t launch_project_f32(int R, int64_t T, int64_t K, uint64_t key, float c, const float *X,
+                              int64_t ldx, void *ws, hipStream_t st);
+hipError_t launch_fold_f32(int R, int64_t T, int64_t D, const float *dY, int64_t lddy, float *S,
+                           int accumulate, const void *ws, hipStream_t st);
+
+// mode 0: rowsq + sqnorm partials; mode 1: RowAdam update of W (and v).
+struct ApplyArgs {
+    int R = 0;
+    int64_t D = 0, K = 0;
+    uint64_t key = 0;
+    float c = 0.f;
+    const float *S = nullptr;
+    const float *v_in = nullptr;   // mode 0
+    float *v = nullptr;            // mode 1 (in/out)
+    const float *rowsq_in = nullptr;
+    float *rowsq_out = nullptr;
+    float *partials = nullptr;
+    float beta2 = 0.f, eps = 0.f, lr_scale = 0.f;
+    void *W = nullptr;
+    int w_bf16 = 0;
+    int64_t ldw = 0;
+};
+
+hipError_t launch_apply_bf16(int mode, const ApplyArgs &a, hipStream_t st);
+hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);
+hipError_t launch_sqnorm_final(const float *partials, int n, float *out, hipStream_t st);
+
+}  // namespace logra

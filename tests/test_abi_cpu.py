@@ -1,0 +1,115 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/logra.h declares, and its host-side validation answers without
+touching a GPU (every call below returns before any kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rank_gradient_sketching_sketch_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from rank_gradient_sketching_sketch_amd import build_lib
+        build_lib.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(logra_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_entry_points_and_helpers():
+    names = declared_functions()
+    for n in ("logra_sketch_accumulate", "logra_update_sqnorm", "logra_rowadam_apply",
+              "logra_sign_words", "logra_sketch_workspace_bytes", "logra_sqnorm_workspace_bytes",
+              "logra_abi_version", "logra_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    from rank_gradient_sketching_sketch_amd import binding as B
+    assert B.logra_abi_version() == 1
+    assert B.logra_status_string(0) == "LOGRA_OK"
+    assert B.logra_status_string(3) == "LOGRA_ERR_WORKSPACE"
+    assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
+
+
+def _m(d=64, k=128, r=32):
+    from rank_gradient_sketching_sketch_amd import binding as B
+    return B.MatrixDesc(d, k, r, 0, 0, 0)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced by the validation paths
+
+
+def test_validation_errors_return_before_launch(lib):
+    m = _m()
+    r = ctypes.byref
+    # null descriptor / null S
+    assert lib.logra_sketch_accumulate(None, 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, None, 0, FAKE, 1 << 20, None) == 1
+    # negative T, ld < cols, misaligned pointer
+    assert lib.logra_sketch_accumulate(r(m), -1, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 100, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, ctypes.c_void_p(0x10002), 128, FAKE, 64, FAKE, 0,
+                                       FAKE, 1 << 20, None) == 1
+    # unsupported rank / dtype / shape on the bf16 path
+    m48 = _m(r=48)
+    assert lib.logra_sketch_accumulate(r(m48), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 2
+    assert lib.logra_sketch_accumulate(r(m), 4, 7, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 2
+    m_odd = _m(d=60)
+    assert lib.logra_sketch_accumulate(r(m_odd), 4, 1, FAKE, 128, FAKE, 60, FAKE, 0, FAKE, 1 << 20, None) == 2
+    # workspace too small / missing
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 16, None) == 3
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, None, 1 << 20, None) == 3
+    # T == 0 with accumulate: nothing to do, no launch
+    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None) == 0
+    # apply passes: beta2 out of range, eps < 0, nulls, unsupported
+    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(1.5), ctypes.c_float(1e-8),
+                                   FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(-1.0),
+                                   FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
+                                   FAKE, None, FAKE, 1 << 20, None) == 1
+    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
+                                   FAKE, FAKE, FAKE, 0, None) == 3
+    assert lib.logra_update_sqnorm(r(m48), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
+                                   FAKE, FAKE, FAKE, 1 << 20, None) == 2
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, FAKE, 1, 100, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(0.9), ctypes.c_float(1e-8), None) == 1
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, FAKE, 5, 128, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(0.9), ctypes.c_float(1e-8), None) == 2
+    assert lib.logra_sign_words(None, FAKE, None) == 1
+
+
+def test_workspace_sizes(lib):
+    from rank_gradient_sketching_sketch_amd import binding as B
+    m = B.MatrixDesc(18944, 3584, 256)
+    ws = B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_BF16)
+    # split partials (fp32) + the projected microbatch (bf16), both T x r
+    assert ws >= 4096 * 256 * (4 + 2) and ws % 16 == 0
+    assert B.logra_sketch_workspace_bytes(m, 0, B.LOGRA_BF16) == 0
+    assert B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_F32) == 4096 * 256 * 4
+    assert B.logra_sketch_workspace_bytes(B.MatrixDesc(64, 64, 48), 16, B.LOGRA_BF16) == 0
+    assert B.logra_sqnorm_workspace_bytes(m, B.LOGRA_BF16) == 4 * ((18944 + 63) // 64)
+
+
+def test_state_size_is_d_by_r():
+    # The sketch state the library keeps per matrix is S (d x r fp32) and v
+    # (d fp32): k/r times smaller than a d x k fp32 gradient.
+    d, k, r = 18944, 3584, 256
+    state = 4 * d * r + 4 * d
+    dense = 4 * d * k
+    assert abs(dense / (4 * d * r) - k / r) < 1e-12 and state < dense / 13

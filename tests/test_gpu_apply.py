@@ -1,0 +1,142 @@
+"""GPU parity of the apply passes: logra_update_sqnorm (pass 1) and
+logra_rowadam_apply (pass 2) through the C ABI against the CPU oracle.
+
+S, v and W are seeded inputs shared by both sides. rowsq, v', sqnorm and the
+W update are compared at 2e-2 (bf16 MFMA compute) or 1e-5 (fp32 compute);
+bf16 W within one bf16 ulp, plus an fp32-W shadow run of the same step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_gradient_sketching_sketch_amd import binding as B
+from rank_gradient_sketching_sketch_amd import inputs
+from gpu_util import (BF16_TOL, F32_TOL, bf16_ulp, device, rel_err, rownorm_err, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _state(seed, d, k, r, s_std=1e-2):
+    g = inputs.generator("apply-state", seed, d, k, r)
+    S = torch.randn(d, r, generator=g) * s_std
+    v = 1e-10 + torch.rand(d, generator=g) * 1e-6
+    W = torch.randn(d, k, generator=g) * 0.02
+    return S, v, W
+
+
+def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev):
+    S_d, v_d, W_d = S.to(dev), v.clone().to(dev), W.clone().to(dev)
+    rowsq = torch.empty(m.d, dtype=torch.float32, device=dev)
+    sq = torch.empty(1, dtype=torch.float32, device=dev)
+    B.logra_update_sqnorm(m, compute, S_d, v_d, beta2, eps, rowsq, sq)
+    torch.cuda.synchronize()
+    rowsq_h, sq_h = rowsq.cpu(), sq.item()
+    B.logra_rowadam_apply(m, compute, S_d, v_d, rowsq, W_d, lr, scale, beta2, eps)
+    torch.cuda.synchronize()
+    return rowsq_h, sq_h, v_d.cpu(), W_d.cpu()
+
+
+APPLY_CASES = [
+    # d, k, r
+    (64, 128, 32),
+    (200, 520, 64),
+    (136, 1000, 128),
+    (520, 1544, 256),
+    (8, 8, 256),
+    (1032, 4104, 256),
+]
+
+
+@pytest.mark.parametrize("d,k,r", APPLY_CASES)
+@pytest.mark.parametrize("wdt", [torch.float32, torch.bfloat16])
+def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
+    dev = device()
+    say("apply bf16", d, k, r, wdt)
+    m = B.MatrixDesc(d, k, r, seed=2, step=d, matrix_id=k)
+    S, v, W = _state(d + k, d, k, r)
+    W = W.to(wdt)
+    lr, scale, beta2, eps = 1e-3, 0.8, 0.999, 1e-8
+    rowsq, sq, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, W, lr, scale, beta2, eps, dev)
+    A = oracle.sign_matrix(2, d, k, r, k)
+    ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
+                              beta2=beta2, eps=eps, lr=lr, scale=scale)
+    e_rq = rel_err(rowsq.double().numpy(), ref["rowsq"])
+    e_v = rel_err(v_new.double().numpy(), ref["v_new"])
+    e_sq = abs(sq / ref["sqnorm"] - 1)
+    say("  rowsq %.2e v %.2e sqnorm %.2e" % (e_rq, e_v, e_sq))
+    assert e_rq < BF16_TOL and e_v < BF16_TOL and e_sq < BF16_TOL
+    W0 = W.double().numpy()
+    if wdt == torch.float32:
+        e_w = rownorm_err(W_new.double().numpy() - W0, ref["W_new"] - W0)
+        say("  dW %.2e" % e_w)
+        assert e_w < BF16_TOL
+    else:
+        W_ref_b = torch.from_numpy(ref["W_new"]).to(torch.bfloat16).double().numpy()
+        diff = np.abs(W_new.double().numpy() - W_ref_b)
+        assert np.all(diff <= bf16_ulp(W_ref_b))
+
+
+@pytest.mark.parametrize("d,k,r", [(256, 512, 32), (45, 130, 20), (300, 65, 1), (64, 256, 100),
+                                   (17, 9, 1024)])
+def test_apply_f32_compute_matches_oracle(d, k, r):
+    dev = device()
+    say("apply f32", d, k, r)
+    m = B.MatrixDesc(d, k, r, seed=4, step=1, matrix_id=r)
+    S, v, W = _state(3 * d + r, d, k, r)
+    lr, scale, beta2, eps = 1e-3, 1.0, 0.999, 1e-8
+    rowsq, sq, v_new, W_new = _run(m, B.LOGRA_F32, S, v, W, lr, scale, beta2, eps, dev)
+    A = oracle.sign_matrix(4, 1, r, r, k)
+    ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
+                              beta2=beta2, eps=eps, lr=lr, scale=scale)
+    e_rq = rel_err(rowsq.double().numpy(), ref["rowsq"])
+    e_v = rel_err(v_new.double().numpy(), ref["v_new"])
+    e_sq = abs(sq / ref["sqnorm"] - 1)
+    W0 = W.double().numpy()
+    e_w = rownorm_err(W_new.double().numpy() - W0, ref["W_new"] - W0)
+    say("  rowsq %.2e v %.2e sqnorm %.2e dW %.2e" % (e_rq, e_v, e_sq, e_w))
+    assert max(e_rq, e_v, e_sq, e_w) < F32_TOL
+
+
+@pytest.mark.parametrize("compute", [B.LOGRA_BF16, B.LOGRA_F32])
+def test_one_hot_S_exposes_signs_through_apply(compute):
+    # S row i = e_{i mod r}: Ghat row i = c * Sigma[i mod r], rowsq = k/r exactly,
+    # and the sign of each W update is the sign of that Sigma entry.
+    dev = device()
+    d, k, r = 320, 392, 64
+    m = B.MatrixDesc(d, k, r, seed=8, step=8, matrix_id=8)
+    S = torch.zeros(d, r)
+    S[torch.arange(d), torch.arange(d) % r] = 1.0
+    v = torch.zeros(d)
+    W = torch.zeros(d, k)
+    rowsq, sq, v_new, W_new = _run(m, compute, S, v, W, 1.0, 1.0, 0.0, 0.0, dev)
+    assert torch.all(rowsq == k / r)
+    A = oracle.sign_matrix(8, 8, 8, r, k)
+    expect = -np.sign(A[np.arange(d) % r])
+    assert np.array_equal(np.sign(W_new.double().numpy()), expect)
+
+
+def test_scale_zero_and_beta2_one_special_cases():
+    dev = device()
+    d, k, r = 128, 256, 256
+    m = B.MatrixDesc(d, k, r, 1, 1, 1)
+    S, v, W = _state(9, d, k, r)
+    for wdt in (torch.float32, torch.bfloat16):
+        Wt = W.to(wdt)
+        _, _, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, Wt, 1e-3, 0.0, 0.999, 1e-8, dev)
+        assert torch.equal(W_new, Wt)
+    _, _, v_new, _ = _run(m, B.LOGRA_BF16, S, v, W, 1e-3, 1.0, 1.0, 1e-8, dev)
+    assert torch.equal(v_new, v)
+
+
+def test_apply_deterministic_and_nan_propagates():
+    dev = device()
+    d, k, r = 256, 1024, 256
+    m = B.MatrixDesc(d, k, r, 5, 5, 5)
+    S, v, W = _state(11, d, k, r)
+    a = _run(m, B.LOGRA_BF16, S, v, W, 1e-3, 1.0, 0.99, 1e-8, dev)
+    b = _run(m, B.LOGRA_BF16, S, v, W, 1e-3, 1.0, 0.99, 1e-8, dev)
+    assert torch.equal(a[0], b[0]) and a[1] == b[1] and torch.equal(a[3], b[3])
+    S[7, 3] = float("nan")
+    rowsq, sq, _, _ = _run(m, B.LOGRA_BF16, S, v, W, 1e-3, 1.0, 0.99, 1e-8, dev)
+    assert np.isnan(sq) and torch.isnan(rowsq[7]) and not torch.isnan(rowsq[8])

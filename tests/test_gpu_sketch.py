@@ -1,0 +1,195 @@
+"""GPU parity of the sketch path: logra_sign_words and logra_sketch_accumulate
+through the C ABI against the CPU oracle, on the same seeded inputs.
+
+Sign words and indexing are bit-exact. S is compared per row (normwise) at
+2e-2 for bf16 inputs and 1e-5 for fp32 inputs. Shapes span several tiles of
+every kernel and ragged tails in T, d and k.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_gradient_sketching_sketch_amd import binding as B
+from rank_gradient_sketching_sketch_amd import inputs
+from gpu_util import BF16_TOL, F32_TOL, device, rownorm_err, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("seed,step,mid,r,k", [
+    (0, 0, 0, 32, 512), (1, 7, 3, 256, 3584), (2**63 + 5, 2**40, 12345, 64, 200),
+    (9, 1, 1, 1, 1), (5, 9, 196, 1024, 130)])
+def test_sign_words_bit_exact(seed, step, mid, r, k):
+    dev = device()
+    say("sign_words", seed, step, mid, r, k)
+    nb = (k + 63) // 64
+    m = B.MatrixDesc(8, k, r, seed, step, mid)
+    words = torch.zeros(r * nb, dtype=torch.int64, device=dev)
+    B.logra_sign_words(m, words)
+    torch.cuda.synchronize()
+    got = words.cpu().numpy().view(np.uint64).reshape(r, nb)
+    assert np.array_equal(got, oracle.sign_words(seed, step, mid, r, k))
+
+
+def _run_sketch(m, X_list, dY_list, dev):
+    S = torch.full((m.d, m.r), float("nan"), dtype=torch.float32, device=dev)
+    for n, (X, dY) in enumerate(zip(X_list, dY_list)):
+        B.logra_sketch_accumulate(m, X.to(dev), dY.to(dev), S, accumulate=n > 0)
+    torch.cuda.synchronize()
+    return S
+
+
+def _ref_sketch(m, X_list, dY_list, rows=None):
+    A = oracle.sign_matrix(m.seed, m.step, m.matrix_id, m.r, m.k)
+    return oracle.sketch([x.double().numpy() for x in X_list], [y.double().numpy() for y in dY_list],
+                         A, rows=rows)
+
+
+BF16_CASES = [
+    # T, d, k, r, microbatches
+    (96, 192, 320, 32, 2),
+    (300, 136, 520, 64, 3),
+    (257, 264, 1000, 128, 2),
+    (1000, 520, 1544, 256, 2),
+    (130, 72, 72, 256, 1),
+    (8, 8, 8, 256, 1),
+    (513, 1032, 4104, 256, 1),
+]
+
+
+@pytest.mark.parametrize("T,d,k,r,mbs", BF16_CASES)
+def test_sketch_bf16_matches_oracle(T, d, k, r, mbs):
+    dev = device()
+    say("sketch bf16", T, d, k, r, mbs)
+    m = B.MatrixDesc(d, k, r, seed=3, step=T, matrix_id=d)
+    X_list, dY_list = [], []
+    for n in range(mbs):
+        X, dY = inputs.random_case(1000 * T + n, T, d, k, dtype=torch.bfloat16, dy_std=1e-2,
+                                   outlier_cols=max(1, k // 100))
+        X_list.append(X)
+        dY_list.append(dY)
+    S = _run_sketch(m, X_list, dY_list, dev)
+    ref = _ref_sketch(m, X_list, dY_list)
+    err = rownorm_err(to_f64(S), ref)
+    say("  S rownorm err %.3e" % err)
+    assert err < BF16_TOL
+
+
+F32_CASES = [
+    (128, 256, 512, 32, 4),     # the tiny fp32 workload's shape
+    (77, 45, 130, 20, 2),
+    (33, 300, 65, 1, 1),
+    (200, 64, 256, 100, 2),
+    (5, 3, 1, 7, 3),
+]
+
+
+@pytest.mark.parametrize("T,d,k,r,mbs", F32_CASES)
+def test_sketch_f32_matches_oracle(T, d, k, r, mbs):
+    dev = device()
+    say("sketch f32", T, d, k, r, mbs)
+    m = B.MatrixDesc(d, k, r, seed=1, step=2, matrix_id=3)
+    X_list, dY_list = [], []
+    for n in range(mbs):
+        X, dY = inputs.random_case(7 * T + n, T, d, k, dtype=torch.float32, dy_std=1e-3)
+        X_list.append(X)
+        dY_list.append(dY)
+    S = _run_sketch(m, X_list, dY_list, dev)
+    ref = _ref_sketch(m, X_list, dY_list)
+    err = rownorm_err(to_f64(S), ref)
+    say("  S rownorm err %.3e" % err)
+    assert err < F32_TOL
+
+
+@pytest.mark.parametrize("r", [64, 256])
+def test_one_hot_probe_exposes_signs_exactly(r):
+    # X = I (one-hot token rows), dY = I: S = c * Sigma^T exactly (c = 1/sqrt(r)
+    # is a power of two here, so bf16 P and fp32 S are exact).
+    dev = device()
+    n = 264
+    say("one-hot probe", n, r)
+    m = B.MatrixDesc(n, n, r, seed=77, step=5, matrix_id=9)
+    eye = torch.eye(n, dtype=torch.bfloat16)
+    S = _run_sketch(m, [eye], [eye], dev)
+    A = oracle.sign_matrix(77, 5, 9, r, n)
+    assert np.array_equal(to_f64(S), A.T)
+
+
+def test_accumulate_flag_and_linearity():
+    dev = device()
+    T, d, k, r = 256, 128, 384, 256
+    m = B.MatrixDesc(d, k, r, 0, 1, 2)
+    X1, dY1 = inputs.random_case(1, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    X2, dY2 = inputs.random_case(2, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    S12 = _run_sketch(m, [X1, X2], [dY1, dY2], dev)
+    S_cat = _run_sketch(m, [torch.cat([X1, X2])], [torch.cat([dY1, dY2])], dev)
+    assert rownorm_err(to_f64(S12), to_f64(S_cat)) < BF16_TOL
+    # accumulate=0 overwrites whatever S held
+    S = torch.randn(d, r, device=dev)
+    B.logra_sketch_accumulate(m, X1.to(dev), dY1.to(dev), S, accumulate=False)
+    S1 = _run_sketch(m, [X1], [dY1], dev)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S1)
+
+
+def test_deterministic_repeat():
+    dev = device()
+    T, d, k, r = 700, 392, 1032, 256
+    m = B.MatrixDesc(d, k, r, 4, 4, 4)
+    X, dY = inputs.random_case(44, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    a = _run_sketch(m, [X, X], [dY, dY], dev)
+    b = _run_sketch(m, [X, X], [dY, dY], dev)
+    assert torch.equal(a, b)
+
+
+def test_empty_microbatch_and_zero_gradient():
+    dev = device()
+    d, k, r = 64, 128, 32
+    m = B.MatrixDesc(d, k, r, 0, 0, 0)
+    S0 = torch.randn(d, r, device=dev)
+    S = S0.clone()
+    empty_x = torch.zeros(0, k, dtype=torch.bfloat16, device=dev)
+    empty_y = torch.zeros(0, d, dtype=torch.bfloat16, device=dev)
+    B.logra_sketch_accumulate(m, empty_x, empty_y, S, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    B.logra_sketch_accumulate(m, empty_x, empty_y, S, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0
+    S = S0.clone()
+    X, _ = inputs.random_case(3, 40, d, k, dtype=torch.bfloat16)
+    B.logra_sketch_accumulate(m, X.to(dev), torch.zeros(40, d, dtype=torch.bfloat16, device=dev), S,
+                              accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+
+
+def test_nan_in_gradient_propagates():
+    dev = device()
+    T, d, k, r = 64, 64, 128, 32
+    m = B.MatrixDesc(d, k, r, 0, 0, 0)
+    X, dY = inputs.random_case(5, T, d, k, dtype=torch.bfloat16)
+    dY[3, 17] = float("nan")
+    S = _run_sketch(m, [X], [dY], dev)
+    bad = torch.isnan(S).any(dim=1).cpu()
+    assert bad[17].item() and bad.sum().item() == 1
+
+
+def test_errors_leave_outputs_untouched():
+    dev = device()
+    T, d, k, r = 64, 64, 128, 32
+    m = B.MatrixDesc(d, k, r, 0, 0, 0)
+    X, dY = inputs.random_case(5, T, d, k, dtype=torch.bfloat16)
+    S0 = torch.randn(d, r, device=dev)
+    S = S0.clone()
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(B.LograError) as e:
+        B.logra_sketch_accumulate(m, X.to(dev), dY.to(dev), S, accumulate=False, ws=ws)
+    assert e.value.status == 3
+    bad_m = B.MatrixDesc(d, k, 48, 0, 0, 0)
+    with pytest.raises(B.LograError) as e:
+        B.logra_sketch_accumulate(bad_m, X.to(dev), dY.to(dev), torch.zeros(d, 48, device=dev), False)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
