@@ -3,7 +3,8 @@ logra_rowadam_apply (pass 2) through the C ABI against the CPU oracle.
 
 S, v and W are seeded inputs shared by both sides. rowsq, v', sqnorm and the
 W update are compared at 2e-2 (bf16 MFMA compute) or 1e-5 (fp32 compute);
-bf16 W within one bf16 ulp, plus an fp32-W shadow run of the same step.
+bf16 W within one bf16 ulp plus the update tolerance (see gpu_util), and an
+fp32-W shadow run of the same step.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 import oracle
 from rank_gradient_sketching_sketch_amd import binding as B
 from rank_gradient_sketching_sketch_amd import inputs
-from gpu_util import (BF16_TOL, F32_TOL, bf16_ulp, device, rel_err, rownorm_err, say, to_f64)
+from gpu_util import (BF16_TOL, F32_TOL, bf16_w_check, device, f32, rel_err, say, to_f64,
+                      w_update_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +62,7 @@ def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
     rowsq, sq, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, W, lr, scale, beta2, eps, dev)
     A = oracle.sign_matrix(2, d, k, r, k)
     ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
-                              beta2=beta2, eps=eps, lr=lr, scale=scale)
+                              beta2=f32(beta2), eps=f32(eps), lr=f32(lr), scale=f32(scale))
     e_rq = rel_err(rowsq.double().numpy(), ref["rowsq"])
     e_v = rel_err(v_new.double().numpy(), ref["v_new"])
     e_sq = abs(sq / ref["sqnorm"] - 1)
@@ -68,13 +70,13 @@ def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
     assert e_rq < BF16_TOL and e_v < BF16_TOL and e_sq < BF16_TOL
     W0 = W.double().numpy()
     if wdt == torch.float32:
-        e_w = rownorm_err(W_new.double().numpy() - W0, ref["W_new"] - W0)
+        e_w = w_update_err(W_new.double().numpy(), ref["W_new"], W0)
         say("  dW %.2e" % e_w)
         assert e_w < BF16_TOL
     else:
-        W_ref_b = torch.from_numpy(ref["W_new"]).to(torch.bfloat16).double().numpy()
-        diff = np.abs(W_new.double().numpy() - W_ref_b)
-        assert np.all(diff <= bf16_ulp(W_ref_b))
+        ok, worst = bf16_w_check(W_new.double().numpy(), ref["W_new"], W0)
+        say("  bf16 W worst error / allowed %.3f" % worst)
+        assert ok
 
 
 @pytest.mark.parametrize("d,k,r", [(256, 512, 32), (45, 130, 20), (300, 65, 1), (64, 256, 100),
@@ -88,12 +90,12 @@ def test_apply_f32_compute_matches_oracle(d, k, r):
     rowsq, sq, v_new, W_new = _run(m, B.LOGRA_F32, S, v, W, lr, scale, beta2, eps, dev)
     A = oracle.sign_matrix(4, 1, r, r, k)
     ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
-                              beta2=beta2, eps=eps, lr=lr, scale=scale)
+                              beta2=f32(beta2), eps=f32(eps), lr=f32(lr), scale=f32(scale))
     e_rq = rel_err(rowsq.double().numpy(), ref["rowsq"])
     e_v = rel_err(v_new.double().numpy(), ref["v_new"])
     e_sq = abs(sq / ref["sqnorm"] - 1)
     W0 = W.double().numpy()
-    e_w = rownorm_err(W_new.double().numpy() - W0, ref["W_new"] - W0)
+    e_w = w_update_err(W_new.double().numpy(), ref["W_new"], W0)
     say("  rowsq %.2e v %.2e sqnorm %.2e dW %.2e" % (e_rq, e_v, e_sq, e_w))
     assert max(e_rq, e_v, e_sq, e_w) < F32_TOL
 

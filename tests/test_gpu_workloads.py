@@ -14,7 +14,8 @@ import torch
 import oracle
 from rank_gradient_sketching_sketch_amd import binding as B
 from rank_gradient_sketching_sketch_amd import inputs
-from gpu_util import BF16_TOL, F32_TOL, bf16_ulp, device, rel_err, rownorm_err, say, to_f64
+from gpu_util import (BF16_TOL, F32_TOL, bf16_w_check, device, f32, rel_err, rownorm_err, say,
+                      to_f64, w_update_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,12 +31,14 @@ def _code(dt):
     return B.LOGRA_BF16 if dt == torch.bfloat16 else B.LOGRA_F32
 
 
-def _step_and_check(wl, spec, step, state, dev, mbs, T, nrows, tol, data_seed=0):
-    """One optimizer step on the GPU and on the oracle (sampled rows); checks
-    S, rowsq, v', the W update and the sqnorm identity; returns the new state."""
+def _step_and_check(wl, spec, step, st, dev, mbs, T, tol, data_seed=0):
+    """One optimizer step on the GPU and on the oracle (sampled rows st["rows"]);
+    checks S, rowsq, v', the W update and the sqnorm identity. Each side
+    carries its own state (W, v) from step to step; the oracle's W is kept at
+    the stored dtype (rounded to bf16 for bf16 W), as the step stores it."""
     d, k, r = spec.d, spec.k, wl.r
+    rows = st["rows"]
     m = B.MatrixDesc(d, k, r, seed=data_seed, step=step, matrix_id=spec.matrix_id)
-    rows = _rows(d, nrows, 1000 * step + spec.matrix_id)
     A = oracle.sign_matrix(data_seed, step, spec.matrix_id, r, k)
     S = torch.empty(d, r, dtype=torch.float32, device=dev)
     ws = torch.empty(max(16, B.logra_sketch_workspace_bytes(m, T, _code(wl.act_dtype))),
@@ -49,54 +52,63 @@ def _step_and_check(wl, spec, step, state, dev, mbs, T, nrows, tol, data_seed=0)
         S_ref = oracle.sketch_rows(dY.double().numpy(), P, rows=rows, S_rows=S_ref,
                                    accumulate=mb > 0)
     torch.cuda.synchronize()
-    S_h = to_f64(S)
-    e_s = rownorm_err(S_h[rows], S_ref)
+    e_s = rownorm_err(to_f64(S)[rows], S_ref)
 
-    W, v, W32 = state
     beta2, eps, lr = wl.beta2, wl.eps, wl.lr
     scale = inputs.step_scale(wl, spec, step, data_seed)
+    hp = dict(beta2=f32(beta2), eps=f32(eps), lr=f32(lr), scale=f32(scale))
     compute = _code(wl.act_dtype)
+    W, v, W32 = st["W"], st["v"], st["W32"]
     rowsq = torch.empty(d, dtype=torch.float32, device=dev)
     sq = torch.empty(1, dtype=torch.float32, device=dev)
+    v_gpu_old = v.clone()
     B.logra_update_sqnorm(m, compute, S, v, beta2, eps, rowsq, sq)
     torch.cuda.synchronize()
-    rowsq_h = to_f64(rowsq)
-    v_old = to_f64(v)
-    # sqnorm identity over all rows, from the GPU's own rowsq and v
-    vn = beta2 * v_old + (1 - beta2) * rowsq_h / k
-    ident = float((rowsq_h / (np.sqrt(vn) + eps) ** 2).sum())
+    # sqnorm identity over all rows, from the GPU's own rowsq and v (a property
+    # of the GPU outputs; no oracle input)
+    rowsq_h, v_old_h = to_f64(rowsq), to_f64(v_gpu_old)
+    vn = hp["beta2"] * v_old_h + (1 - hp["beta2"]) * rowsq_h / k
+    ident = float((rowsq_h / (np.sqrt(vn) + hp["eps"]) ** 2).sum())
     e_ident = abs(sq.item() / ident - 1)
-    W_old = to_f64(W)[rows]
-    W32_old = to_f64(W32)[rows] if W32 is not None else None
-    ref = oracle.rowadam_rows(S_ref, A, v_old[rows], W_old, beta2=beta2, eps=eps, lr=lr, scale=scale)
+
+    ref = oracle.rowadam_rows(S_ref, A, st["v_ref"], st["W_ref"], **hp)
     e_rq = rel_err(rowsq_h[rows], ref["rowsq"])
     B.logra_rowadam_apply(m, compute, S, v, rowsq, W, lr, scale, beta2, eps)
     if W32 is not None:
-        v_sh = torch.from_numpy(v_old).float().to(dev)
-        B.logra_rowadam_apply(m, compute, S, v_sh, rowsq, W32, lr, scale, beta2, eps)
+        B.logra_rowadam_apply(m, compute, S, v_gpu_old, rowsq, W32, lr, scale, beta2, eps)
     torch.cuda.synchronize()
     e_v = rel_err(to_f64(v)[rows], ref["v_new"])
     W_new = to_f64(W)[rows]
     if W.dtype == torch.bfloat16:
-        W_ref_b = torch.from_numpy(ref["W_new"]).to(torch.bfloat16).double().numpy()
-        w_ok = bool(np.all(np.abs(W_new - W_ref_b) <= bf16_ulp(W_ref_b)))
-        ref32 = oracle.rowadam_rows(S_ref, A, v_old[rows], W32_old, beta2=beta2, eps=eps, lr=lr,
-                                    scale=scale)
-        e_w = rownorm_err(to_f64(W32)[rows] - W32_old, ref32["W_new"] - W32_old)
+        w_ok, _ = bf16_w_check(W_new, ref["W_new"], st["W_ref"], steps=step + 1)
+        ref32 = oracle.rowadam_rows(S_ref, A, st["v_ref"], st["W32_ref"], **hp)
+        e_w = w_update_err(to_f64(W32)[rows], ref32["W_new"], st["W32_ref"])
+        st["W32_ref"] = ref32["W_new"]
+        st["W_ref"] = torch.from_numpy(ref["W_new"]).to(torch.bfloat16).double().numpy()
     else:
         w_ok = True
-        e_w = rownorm_err(W_new - W_old, ref["W_new"] - W_old)
-    say("  %s step %d: S %.2e rowsq %.2e v %.2e dW %.2e sqnorm-identity %.2e W-ulp %s"
+        e_w = w_update_err(W_new, ref["W_new"], st["W_ref"])
+        st["W_ref"] = ref["W_new"]
+    st["v_ref"] = ref["v_new"]
+    say("  %s step %d: S %.2e rowsq %.2e v %.2e dW %.2e sqnorm-identity %.2e W-bf16 %s"
         % (spec.name, step, e_s, e_rq, e_v, e_w, e_ident, w_ok))
     assert e_s < tol and e_rq < tol and e_v < tol and e_w < tol and e_ident < tol and w_ok
-    return W, v, W32
+    return st
 
 
-def _init_state(wl, spec, dev, shadow):
-    W = inputs.weights(wl, spec).to(dev)
-    v = inputs.second_moment(wl, spec).to(dev)
-    W32 = W.float().clone() if (shadow and W.dtype == torch.bfloat16) else None
-    return W, v, W32
+def _init_state(wl, spec, dev, shadow, nrows):
+    """GPU state from the input generator, and the oracle's copy of the same
+    generated values on the sampled rows."""
+    W_h = inputs.weights(wl, spec)
+    v_h = inputs.second_moment(wl, spec)
+    rows = _rows(spec.d, nrows, spec.matrix_id)
+    st = {"rows": rows, "W": W_h.to(dev), "v": v_h.to(dev), "W32": None,
+          "W_ref": W_h.double().numpy()[rows], "v_ref": v_h.double().numpy()[rows],
+          "W32_ref": None}
+    if shadow and W_h.dtype == torch.bfloat16:
+        st["W32"] = W_h.float().to(dev)
+        st["W32_ref"] = W_h.double().numpy()[rows]
+    return st
 
 
 def test_tiny_fp32_workload_full():
@@ -104,8 +116,8 @@ def test_tiny_fp32_workload_full():
     wl = inputs.WORKLOADS["tiny_fp32"]
     spec = wl.matrices[0]
     say("workload tiny_fp32", spec)
-    state = _init_state(wl, spec, dev, shadow=False)
-    _step_and_check(wl, spec, 0, state, dev, wl.microbatches, wl.tokens, None, F32_TOL)
+    st = _init_state(wl, spec, dev, shadow=False, nrows=None)
+    _step_and_check(wl, spec, 0, st, dev, wl.microbatches, wl.tokens, F32_TOL)
 
 
 def test_qwen15b_set_all_projections():
@@ -113,8 +125,8 @@ def test_qwen15b_set_all_projections():
     wl = inputs.WORKLOADS["qwen1.5b_set"]
     for spec in wl.matrices:
         say("workload qwen1.5b_set", spec)
-        state = _init_state(wl, spec, dev, shadow=True)
-        _step_and_check(wl, spec, 0, state, dev, 2, wl.tokens, 256, BF16_TOL)
+        st = _init_state(wl, spec, dev, shadow=True, nrows=256)
+        _step_and_check(wl, spec, 0, st, dev, 2, wl.tokens, BF16_TOL)
 
 
 def test_qwen7b_up_two_steps_full_microbatches():
@@ -123,10 +135,10 @@ def test_qwen7b_up_two_steps_full_microbatches():
     dev = device()
     wl = inputs.WORKLOADS["qwen7b_up"]
     spec = wl.matrices[0]
-    state = _init_state(wl, spec, dev, shadow=True)
+    st = _init_state(wl, spec, dev, shadow=True, nrows=512)
     for step in range(2):
         say("workload qwen7b_up step", step)
-        state = _step_and_check(wl, spec, step, state, dev, wl.microbatches, wl.tokens, 512, BF16_TOL)
+        st = _step_and_check(wl, spec, step, st, dev, wl.microbatches, wl.tokens, BF16_TOL)
 
 
 @pytest.mark.parametrize("name", ["qwen7b_28layer", "27b_64layer"])
@@ -137,5 +149,5 @@ def test_one_layer_of_large_stacks(name):
     wl = inputs.WORKLOADS[name]
     for spec in wl.matrices[:7]:
         say("workload", name, spec)
-        state = _init_state(wl, spec, dev, shadow=True)
-        _step_and_check(wl, spec, 0, state, dev, 1, wl.tokens, 256, BF16_TOL)
+        st = _init_state(wl, spec, dev, shadow=True, nrows=256)
+        _step_and_check(wl, spec, 0, st, dev, 1, wl.tokens, BF16_TOL)
