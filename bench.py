@@ -40,7 +40,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen7b_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of known size: the HBM byte counters of
+    a profiler read on it give the factor that converts their readings on
+    the library's kernels into bytes."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 def cpu_model():
@@ -59,6 +76,10 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
     from rank_gradient_sketching_sketch_amd import binding as B

@@ -21,6 +21,21 @@ struct Stage1Plan {
 };
 
 Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R);
+
+// Work split of the fold S (+)= dY^T P (bf16 path): n_wg_d workgroups over the
+// nblk 16-row blocks of S, times n_split ranges of steps_per 32-token steps.
+// With n_split > 1 the partial tiles (n_split x d x r fp32) go to the workspace.
+struct FoldPlan {
+    int nblk = 0;
+    int n_wg_d = 0;
+    int n_split = 0;
+    int steps_per = 0;
+    size_t part_bytes = 0;
+};
+FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
+hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
+                                  const uint16_t *P, int p_blocks, float *S, int accumulate,
+                                  float *part, hipStream_t st);
 size_t workspace_sketch_f32(int64_t T, int64_t R);
 int apply_blocks_bf16(int64_t D);
 int apply_blocks_f32(int64_t D);

@@ -15,13 +15,8 @@
 //             the workspace and a finalize pass adds them in a fixed order,
 //             scales by c and rounds P to bf16 (nearest even) in a layout whose
 //             16-byte chunks are exactly the stage-2 operand fragments.
-//   stage 2   S (+)= dY^T P  (d x r, contraction over the tokens). dY is
-//             token-major, so each lane loads 8 bytes (4 columns) from 8
-//             consecutive token rows and transposes them in registers with
-//             v_perm_b32 into four operand fragments; that makes MFMA row m of
-//             block mb stand for output row d0 + 4m + mb. Each workgroup owns a
-//             row tile and all r columns, so dY is read once from HBM and no
-//             reduction across workgroups is needed.
+//   stage 2   S (+)= dY^T P  (d x r, contraction over the tokens): the fold
+//             kernel in fold_bf16.hip.
 #include "common.hpp"
 #include "launch.hpp"
 #include "signs.hpp"
@@ -160,89 +155,6 @@ __global__ __launch_bounds__(256) void stage1_finalize_kernel(const float *__res
     *reinterpret_cast<u32x4_t *>(P + base) = o;
 }
 
-// ---------------------------------------------------------------- stage 2 --
-template <int R>
-__global__ __launch_bounds__(256) void stage2_bf16_kernel(
-    const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
-    float *__restrict__ S, int accumulate) {
-    using Sh = SketchShape<R>;
-    constexpr int NBW = Sh::NBW;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave / Sh::WN, wn = wave % Sh::WN;
-    const int m = lane & 15, g = lane >> 4;
-    const int d_base = blockIdx.x * (Sh::WM * 64) + wm * 64;
-    const int l_base = wn * NBW * 16;
-    const int col = d_base + 4 * m;
-    const bool colok = col < D;
-    const uint16_t *dcol = dY + (colok ? col : 0);
-
-    f32x4_t acc[4][NBW];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero_f32x4();
-
-    const int nsteps = (T + 31) >> 5;
-    u32x2_t raw[8];
-    u32x4_t bf[NBW];
-    auto load_step = [&](int s, u32x2_t (&rw)[8], u32x4_t (&b)[NBW]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = (s << 5) + 8 * g + e;
-            rw[e] = (colok && t < T) ? load_u32x2(dcol + static_cast<int64_t>(t) * lddy)
-                                     : u32x2_t{0u, 0u};
-        }
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const int l = l_base + 16 * nb + m;
-            b[nb] = load_u32x4(P + (static_cast<size_t>(s) * R + l) * 32 + 8 * g);
-        }
-    };
-    if (nsteps > 0) load_step(0, raw, bf);
-    for (int s = 0; s < nsteps; ++s) {
-        u32x2_t raw_n[8];
-        u32x4_t bf_n[NBW];
-        if (s + 1 < nsteps) load_step(s + 1, raw_n, bf_n);
-        // 8 tokens x 4 columns -> 4 fragments of 8 tokens each
-        u32x4_t a[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x2_t r0 = raw[2 * q], r1 = raw[2 * q + 1];
-            a[0][q] = join_lo16(r0.x, r1.x);
-            a[1][q] = join_hi16(r0.x, r1.x);
-            a[2][q] = join_lo16(r0.y, r1.y);
-            a[3][q] = join_hi16(r0.y, r1.y);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma_bf16(a[mb], bf[nb], acc[mb][nb]);
-        if (s + 1 < nsteps) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) raw[e] = raw_n[e];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) bf[nb] = bf_n[nb];
-        }
-    }
-
-    // output row of fragment (mb, element e) is d_base + 4*(4g + e) + mb
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = d_base + 4 * (4 * g + e) + mb;
-            if (i < D) {
-                float *srow = S + static_cast<int64_t>(i) * R;
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) {
-                    const int l = l_base + 16 * nb + m;
-                    const float prev = accumulate ? srow[l] : 0.f;
-                    srow[l] = prev + acc[mb][nb][e];
-                }
-            }
-        }
-}
-
 // ----------------------------------------------------------------- plans --
 static int stage1_tile_m(int R) {
     const int nb = R / 16;
@@ -287,13 +199,12 @@ static hipError_t project_bf16_r(int64_t T, int64_t K, uint64_t key, float c, co
 template <int R>
 static hipError_t fold_bf16_r(int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
                               float *S, int accumulate, const void *ws, hipStream_t st) {
-    using Sh = SketchShape<R>;
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
-    const uint16_t *P = reinterpret_cast<const uint16_t *>(static_cast<const char *>(ws) + p.part_bytes);
-    const int rows_per_wg = Sh::WM * 64;
-    hipLaunchKernelGGL(stage2_bf16_kernel<R>, dim3((D + rows_per_wg - 1) / rows_per_wg), dim3(256), 0,
-                       st, dY, lddy, static_cast<int>(T), static_cast<int>(D), P, S, accumulate);
-    return hipGetLastError();
+    const char *base = static_cast<const char *>(ws);
+    const uint16_t *P = reinterpret_cast<const uint16_t *>(base + p.part_bytes);
+    float *part = reinterpret_cast<float *>(const_cast<char *>(base) + p.part_bytes + p.p_bytes);
+    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, static_cast<int>(p.t_pad / 32), S, accumulate,
+                                  part, st);
 }
 
 hipError_t launch_project_bf16(int R, int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
