@@ -30,10 +30,16 @@ logra_status from_hip(hipError_t e) { return e == hipSuccess ? LOGRA_OK : LOGRA_
 
 float inv_sqrt_rank(int64_t r) { return 1.0f / sqrtf(static_cast<float>(r)); }
 
-size_t sqnorm_partials(const logra_matrix *m, int compute_dtype) {
-    const int n = compute_dtype == LOGRA_BF16 ? apply_blocks_bf16(m->d) : apply_blocks_f32(m->d);
-    return static_cast<size_t>(n) * sizeof(float);
+size_t sqnorm_ws_bytes(const logra_matrix *m, int compute_dtype) {
+    if (compute_dtype == LOGRA_BF16) {
+        const SqnormPlan p = plan_sqnorm_bf16(m->d, m->k, static_cast<int>(m->r));
+        return p.partial_bytes + p.gram_bytes;
+    }
+    return static_cast<size_t>(apply_blocks_f32(m->d)) * sizeof(float);
 }
+
+// Buffer views address at most 2^31 bytes.
+bool fits_view(int64_t rows, int64_t ld, int64_t elem) { return rows * ld * elem < (1ll << 31); }
 
 }  // namespace
 
@@ -90,6 +96,7 @@ static logra_status check_project(const logra_matrix *m, int64_t T, int act_dtyp
     if (T == 0) return LOGRA_OK;
     if (!X || ldx < m->k) return LOGRA_ERR_INVALID_ARGUMENT;
     if (act_dtype == LOGRA_BF16 && (ldx % 8 || !aligned16(X))) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype == LOGRA_BF16 && !fits_view(T, ldx, 2)) return LOGRA_ERR_UNSUPPORTED;
     const size_t need = logra_sketch_workspace_bytes(m, T, act_dtype);
     if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
     return LOGRA_OK;
@@ -101,6 +108,8 @@ static logra_status check_fold(const logra_matrix *m, int64_t T, int act_dtype, 
     if (T == 0) return LOGRA_OK;
     if (!dY || lddy < m->d) return LOGRA_ERR_INVALID_ARGUMENT;
     if (act_dtype == LOGRA_BF16 && (lddy % 8 || !aligned16(dY))) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype == LOGRA_BF16 && (!fits_view(T + 32, lddy, 2) || !fits_view(m->d, m->r, 4 * 16)))
+        return LOGRA_ERR_UNSUPPORTED;
     const size_t need = logra_sketch_workspace_bytes(m, T, act_dtype);
     if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
     return LOGRA_OK;
@@ -163,7 +172,7 @@ logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_d
 size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype) {
     if (!matrix_ok(m)) return 0;
     if (compute_dtype != LOGRA_F32 && compute_dtype != LOGRA_BF16) return 0;
-    return sqnorm_partials(m, compute_dtype);
+    return sqnorm_ws_bytes(m, compute_dtype);
 }
 
 static logra_status check_apply_common(const logra_matrix *m, int compute_dtype, const float *S,
@@ -200,17 +209,17 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const
     logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
     if (stt != LOGRA_OK) return stt;
     if (!v || !rowsq || !sqnorm) return LOGRA_ERR_INVALID_ARGUMENT;
-    const size_t need = sqnorm_partials(m, compute_dtype);
-    if (!ws || ws_bytes < need) return LOGRA_ERR_WORKSPACE;
+    const size_t need = sqnorm_ws_bytes(m, compute_dtype);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     ApplyArgs a = base_args(m, S, beta2, eps);
     a.v_in = v;
     a.rowsq_out = rowsq;
+    a.sqnorm = sqnorm;
+    if (compute_dtype == LOGRA_BF16) return from_hip(launch_sqnorm_bf16(a, ws, st));
     a.partials = static_cast<float *>(ws);
-    hipError_t e = compute_dtype == LOGRA_BF16 ? launch_apply_bf16(0, a, st) : launch_apply_f32(0, a, st);
-    if (e != hipSuccess) return LOGRA_ERR_HIP;
-    const int nparts = static_cast<int>(need / sizeof(float));
-    return from_hip(launch_sqnorm_final(a.partials, nparts, sqnorm, st));
+    if (launch_apply_f32(0, a, st) != hipSuccess) return LOGRA_ERR_HIP;
+    return from_hip(launch_sqnorm_final(a.partials, apply_blocks_f32(m->d), sqnorm, st));
 }
 
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const float *S,
@@ -222,6 +231,8 @@ logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const
     if (w_dtype != LOGRA_F32 && w_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
     if (ldw < m->k) return LOGRA_ERR_INVALID_ARGUMENT;
     if (compute_dtype == LOGRA_BF16 && (ldw % 8 || !aligned16(W))) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (compute_dtype == LOGRA_BF16 && !fits_view(m->d, ldw, w_dtype == LOGRA_BF16 ? 2 : 4))
+        return LOGRA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     ApplyArgs a = base_args(m, S, beta2, eps);
     a.v = v;
@@ -230,7 +241,7 @@ logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const
     a.W = W;
     a.w_bf16 = w_dtype == LOGRA_BF16 ? 1 : 0;
     a.ldw = ldw;
-    return from_hip(compute_dtype == LOGRA_BF16 ? launch_apply_bf16(1, a, st)
+    return from_hip(compute_dtype == LOGRA_BF16 ? launch_rowadam_bf16(a, st)
                                                 : launch_apply_f32(1, a, st));
 }
 

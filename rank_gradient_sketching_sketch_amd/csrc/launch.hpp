@@ -37,8 +37,16 @@ hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *d
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   float *part, hipStream_t st);
 size_t workspace_sketch_f32(int64_t T, int64_t R);
-int apply_blocks_bf16(int64_t D);
 int apply_blocks_f32(int64_t D);
+
+// Workspace of apply pass 1 with bf16 compute: per-workgroup partials of the
+// controller's reduction, then the r x r Gram matrix of the signs (bf16).
+struct SqnormPlan {
+    int n_blocks = 0;
+    size_t partial_bytes = 0;
+    size_t gram_bytes = 0;
+};
+SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R);
 
 hipError_t launch_sign_words(uint64_t key, int R, int K, uint64_t *words, hipStream_t st);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t st);
@@ -53,7 +61,7 @@ hipError_t launch_project_f32(int R, int64_t T, int64_t K, uint64_t key, float c
 hipError_t launch_fold_f32(int R, int64_t T, int64_t D, const float *dY, int64_t lddy, float *S,
                            int accumulate, const void *ws, hipStream_t st);
 
-// mode 0: rowsq + sqnorm partials; mode 1: RowAdam update of W (and v).
+// Arguments of the apply passes (pointers are device pointers).
 struct ApplyArgs {
     int R = 0;
     int64_t D = 0, K = 0;
@@ -65,13 +73,20 @@ struct ApplyArgs {
     const float *rowsq_in = nullptr;
     float *rowsq_out = nullptr;
     float *partials = nullptr;
+    float *sqnorm = nullptr;
     float beta2 = 0.f, eps = 0.f, lr_scale = 0.f;
     void *W = nullptr;
     int w_bf16 = 0;
     int64_t ldw = 0;
 };
 
-hipError_t launch_apply_bf16(int mode, const ApplyArgs &a, hipStream_t st);
+// bf16 compute: pass 1 (Gram form, writes rowsq and sqnorm) and pass 2
+// (RowAdam update of W, then v committed).
+hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st);
+hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st);
+hipError_t launch_commit_v(float *v, const float *rowsq, int64_t D, int64_t K, float beta2,
+                           hipStream_t st);
+// fp32 compute: mode 0 = pass 1 (rowsq + partials), mode 1 = pass 2 (W and v).
 hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);
 hipError_t launch_sqnorm_final(const float *partials, int n, float *out, hipStream_t st);
 

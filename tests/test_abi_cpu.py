@@ -103,7 +103,10 @@ def test_workspace_sizes(lib):
     assert B.logra_sketch_workspace_bytes(m, 0, B.LOGRA_BF16) == 0
     assert B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_F32) == 4096 * 256 * 4
     assert B.logra_sketch_workspace_bytes(B.MatrixDesc(64, 64, 48), 16, B.LOGRA_BF16) == 0
-    assert B.logra_sqnorm_workspace_bytes(m, B.LOGRA_BF16) == 4 * ((18944 + 63) // 64)
+    # per-workgroup partials of the controller's reduction + the r x r sign Gram matrix (bf16)
+    sq = B.logra_sqnorm_workspace_bytes(m, B.LOGRA_BF16)
+    assert sq >= 4 * ((18944 + 127) // 128) + 256 * 256 * 2
+    assert B.logra_sqnorm_workspace_bytes(m, B.LOGRA_F32) == 4 * ((18944 + 7) // 8)
 
 
 def test_state_size_is_d_by_r():
