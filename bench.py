@@ -226,7 +226,7 @@ def main():
                   "ms_per_step": round(apply_ms, 4),
                   "sqnorm_ms": round(tot["sqnorm"] / K, 5), "rowadam_ms": round(tot["apply"] / K, 5),
                   "skipped_nonfinite": skipped[0]},
-        "roofline": {"kernel": "stage2_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
+        "roofline": {"kernel": "fold_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
                      "achieved": round(fold_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(fold_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": round(fold_bytes_avg)},
