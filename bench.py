@@ -9,10 +9,12 @@ a step has its own buffers, so the inputs of one step (about 3 GB in the
 default workload) stream through the 256 MB last-level cache.
 
 Prints one JSON line. value = sketch-accumulate TFLOP/s (algorithmic
-2*T*r*(d+k) per microbatch call, over the HIP-event time of the sketch
-calls); the same line carries the RowAdam-apply GB/s, the roofline of the
-dominant kernel (the stage-2 fold) and the CPU oracle timed on a bounded
-sample of the same workload.
+2*T*r*(d+k) per microbatch call, over the HIP-event time of each step's
+sketch phase, one event pair per phase); the same line carries the
+RowAdam-apply GB/s (passes 1 and 2, the device-to-host read excluded), the
+roofline of the dominant kernel (the stage-2 fold, its average launch
+duration from a back-to-back run of the step's fold calls after the timed
+steps) and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -133,6 +135,8 @@ def main():
     apply_bytes_per_step = sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * r + 8.0 * s.d + 8.0 * s.d
                                for s in wl.matrices)
 
+    # Event records cost a few microseconds of GPU time each, so the timed
+    # steps record events only at phase boundaries (sketch | pass 1 | pass 2).
     ev_log = []   # (kind, start_event, end_event)
 
     def ev():
@@ -142,32 +146,32 @@ def main():
 
     skipped = [0]
 
+    def sketch_calls(step, m, mb, what):
+        spec = m["spec"]
+        X = xbuf[(inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)]
+        dY = ybuf[(spec.matrix_id, mb)]
+        if what in ("project", "both"):
+            B.logra_sketch_project(m["desc"], X, ws, stream)
+        if what in ("fold", "both"):
+            B.logra_sketch_fold(m["desc"], dY, m["S"], mb > 0, ws, stream)
+
     def one_step(step, timed):
         for m in mats:
             spec = m["spec"]
-            desc = B.MatrixDesc(spec.d, spec.k, r, seed=0, step=step, matrix_id=spec.matrix_id)
-            m["desc"] = desc
-            for mb in range(nmb):
-                X = xbuf[(inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)]
-                dY = ybuf[(spec.matrix_id, mb)]
-                e0 = ev() if timed else None
-                B.logra_sketch_project(desc, X, ws, stream)
-                e1 = ev() if timed else None
-                B.logra_sketch_fold(desc, dY, m["S"], mb > 0, ws, stream)
-                if timed:
-                    e2 = ev()
-                    ev_log.append(("project", e0, e1))
-                    ev_log.append(("fold", e1, e2))
+            m["desc"] = B.MatrixDesc(spec.d, spec.k, r, seed=0, step=step, matrix_id=spec.matrix_id)
         e0 = ev() if timed else None
+        for m in mats:
+            for mb in range(nmb):
+                sketch_calls(step, m, mb, "both")
+        e1 = ev() if timed else None
         for m in mats:
             B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["rowsq"],
                                   m["sq"], sq_ws, stream)
-        if timed:
-            ev_log.append(("sqnorm", e0, ev()))
+        e2 = ev() if timed else None
         # step controller stand-in: read every sqnorm, skip non-finite ones,
         # use the drawn scale (the controller's formula is not part of this path)
         sqs = torch.cat([m["sq"] for m in mats]).cpu().tolist()
-        e0 = ev() if timed else None
+        e3 = ev() if timed else None
         for m, sq in zip(mats, sqs):
             if not math.isfinite(sq):
                 skipped[0] += 1
@@ -176,7 +180,10 @@ def main():
             B.logra_rowadam_apply(m["desc"], code, m["S"], m["v"], m["rowsq"], m["W"], wl.lr, scale,
                                   wl.beta2, wl.eps, stream)
         if timed:
-            ev_log.append(("apply", e0, ev()))
+            e4 = ev()
+            ev_log.append(("sketch", e0, e1))
+            ev_log.append(("sqnorm", e1, e2))
+            ev_log.append(("apply", e3, e4))
 
     for s in range(args.warmup):
         one_step(s, False)
@@ -187,19 +194,34 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    tot = {"project": 0.0, "fold": 0.0, "sqnorm": 0.0, "apply": 0.0}
-    cnt = {k: 0 for k in tot}
+    # Per-kernel averages for the roofline: each half of the sketch launched
+    # back to back over the same microbatch buffers, one event pair around
+    # the run (the average includes the launch gap between kernels).
+    def per_launch_ms(what):
+        reps = max(1, 64 // (nmb * len(mats)))
+        torch.cuda.synchronize()
+        a = ev()
+        for _ in range(reps):
+            for m in mats:
+                for mb in range(nmb):
+                    sketch_calls(0, m, mb, what)
+        b = ev()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * nmb * len(mats))
+
+    project_ms = per_launch_ms("project")
+    fold_ms = per_launch_ms("fold")
+
+    tot = {"sketch": 0.0, "sqnorm": 0.0, "apply": 0.0}
     for kind, a, b in ev_log:
         tot[kind] += a.elapsed_time(b)
-        cnt[kind] += 1
     K = args.steps
-    sketch_ms = (tot["project"] + tot["fold"]) / K
+    sketch_ms = tot["sketch"] / K
     apply_ms = (tot["sqnorm"] + tot["apply"]) / K
     sketch_tflops = sketch_flop_per_step / (sketch_ms * 1e-3) / 1e12
     apply_gbps = apply_bytes_per_step / (apply_ms * 1e-3) / 1e9
-    fold_avg_ms = tot["fold"] / max(1, cnt["fold"])
     fold_bytes_avg = fold_bytes_per_step / (nmb * len(mats))
-    fold_gbps = fold_bytes_avg / (fold_avg_ms * 1e-3) / 1e9
+    fold_gbps = fold_bytes_avg / (fold_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -220,8 +242,8 @@ def main():
         "sketch": {"tflops": round(sketch_tflops, 2),
                    "frac_mfma_peak": round(sketch_tflops / PEAK_BF16_TFLOPS, 4),
                    "ms_per_step": round(sketch_ms, 4),
-                   "project_ms_per_call": round(tot["project"] / max(1, cnt["project"]), 5),
-                   "fold_ms_per_call": round(fold_avg_ms, 5)},
+                   "project_ms_per_launch": round(project_ms, 5),
+                   "fold_ms_per_launch": round(fold_ms, 5)},
         "apply": {"GBps": round(apply_gbps, 1), "frac_hbm_peak": round(apply_gbps / PEAK_HBM_GBPS, 4),
                   "ms_per_step": round(apply_ms, 4),
                   "sqnorm_ms": round(tot["sqnorm"] / K, 5), "rowadam_ms": round(tot["apply"] / K, 5),

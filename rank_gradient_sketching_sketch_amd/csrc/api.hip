@@ -73,7 +73,7 @@ size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dt
         if (!bf16_rank_ok(m->r)) return 0;
         const Stage1Plan p = plan_stage1_bf16(T, m->k, static_cast<int>(m->r));
         const FoldPlan f = plan_fold_bf16(T, m->d, static_cast<int>(m->r));
-        return p.part_bytes + p.p_bytes + f.part_bytes;
+        return p.p_bytes + f.part_bytes;
     }
     if (act_dtype == LOGRA_F32) return workspace_sketch_f32(T, m->r);
     return 0;

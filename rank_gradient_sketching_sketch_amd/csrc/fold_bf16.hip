@@ -69,8 +69,17 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     int n_wg_d, int steps_per) {
     using Sh = FoldShape<R>;
     constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = kFoldPrefetch;
-    constexpr int kSlot = 32 * kFoldLdsRow;   // one step: 32 token rows
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kFoldSlots * kSlot];
+    constexpr int kSlot = 32 * kFoldLdsRow;             // one step: 32 token rows
+    constexpr int kTileRows = kFoldMaxBlocks * 16;      // rows of S per workgroup (max)
+    constexpr int kTileLd = R + 4;                      // fp32 row stride of the output tile in LDS
+    constexpr int kRowChunks = R / 4;                   // 16-byte chunks per row of S
+    constexpr int kOutChunks = (kTileRows * kRowChunks + 255) / 256;   // per thread
+    constexpr int kRingBytes = kFoldSlots * kSlot * 2;
+    constexpr int kTileBytes = kTileRows * kTileLd * 4;
+    // The dY ring during the loop, the output tile in the epilogue.
+    __shared__ __attribute__((aligned(16))) char smem[kRingBytes > kTileBytes ? kRingBytes : kTileBytes];
+    uint16_t *lds = reinterpret_cast<uint16_t *>(smem);
+    float *tile = reinterpret_cast<float *>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index as a scalar: every per-wave decision below is a scalar branch
@@ -95,14 +104,18 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const int s_end = min(nsteps, s_begin + steps_per);
     const int l_base = wn * NBW * 16;
 
-    // Buffer views: loads past num_records return zero, which masks the token
-    // tail, the phantom steps after s_end and every chunk sent to kOob.
+    // Buffer views: loads past num_records return zero and stores there are
+    // dropped, which masks the token tail, the phantom steps after s_end,
+    // rows past d and every access sent to kOob.
     constexpr uint32_t kOob = 0x80000000u;
     const __amdgpu_buffer_rsrc_t dy_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(dY), 0, static_cast<int>(static_cast<int64_t>(T) * lddy * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(P), 0, static_cast<int>(static_cast<int64_t>(p_blocks) * R * 64),
         0x00020000);
+    float *dst = part ? part + static_cast<size_t>(sp) * D * R : S;
+    const __amdgpu_buffer_rsrc_t s_rs =
+        __builtin_amdgcn_make_buffer_rsrc(dst, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
 
     // The (at most two) 16-byte dY chunks this thread moves per step. Chunk
     // counts are multiples of 64, so whether a wave has a chunk is uniform
@@ -150,6 +163,13 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             a[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
         }
     };
+    // Output chunk c of this thread: row (tid + 256 c) / kRowChunks of the
+    // tile, 4 columns from 4 * ((tid + 256 c) % kRowChunks).
+    auto out_off = [&](int c) -> uint32_t {
+        const int q = tid + 256 * c;
+        const int row = q / kRowChunks, col = 4 * (q % kRowChunks);
+        return row < nmb * 16 ? static_cast<uint32_t>(((d0 + row) * R + col) * 4) : kOob;
+    };
 
     f32x4_t acc[MBW][NBW];
 #pragma unroll
@@ -157,13 +177,27 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[j][nb] = zero_f32x4();
 
+    // Prefetch ring: dY chunks and P fragments of the next PF steps, issued
+    // in step order, so that every wait below is for a load issued PF - 1 or
+    // PF steps earlier (loads complete in issue order).
     u32x4_t raw[PF][2];
+    u32x4_t pb[PF][NBW];
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
+    for (int p = 0; p < PF; ++p) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) raw[p][k] = gload(s_begin + p, k);
+        bload(s_begin + p, pb[p]);
+    }
+    // The old S tile, read while the stream runs (the first waits are for
+    // the loads above, issued before these).
+    const bool add_old = accumulate && !part;
+    u32x4_t old[kOutChunks];
+#pragma unroll
+    for (int c = 0; c < kOutChunks; ++c)
+        old[c] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s_rs, add_old ? out_off(c) : kOob, 0, 0));
 
-    u32x4_t a_cur[MBW], a_nxt[MBW], b_cur[NBW], b_nxt[NBW];
+    u32x4_t a_cur[MBW], a_nxt[MBW];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         lstore(s_begin, raw[0][k], k);
@@ -171,8 +205,6 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     }
     lds_barrier();
     aread(s_begin, a_cur);
-    bload(s_begin, b_cur);
-    bload(s_begin + 1, b_nxt);
 
     // Whole groups of PF steps; up to PF-1 steps past s_end load zeros and
     // add nothing.
@@ -180,7 +212,8 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int s = s0 + p;
-            // raw[(p + 1) % PF] holds step s + 1 (s0 - s_begin is a multiple of PF)
+            // raw[(p + 1) % PF] holds the dY of step s + 1 and pb[p] the P
+            // fragments of step s (s0 - s_begin is a multiple of PF)
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 lstore(s + 1, raw[(p + 1) % PF][k], k);
@@ -188,62 +221,45 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             }
             lds_barrier();
             aread(s + 1, a_nxt);
-            u32x4_t b_nn[NBW];
-            bload(s + 2, b_nn);
 #pragma unroll
             for (int j = 0; j < MBW; ++j) {
                 if (wm + j * WM < nmb) {
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
-                        acc[j][nb] = mfma_bf16(a_cur[j], b_cur[nb], acc[j][nb]);
+                        acc[j][nb] = mfma_bf16(a_cur[j], pb[p][nb], acc[j][nb]);
                 }
             }
+            bload(s + PF, pb[p]);
 #pragma unroll
             for (int j = 0; j < MBW; ++j) a_cur[j] = a_nxt[j];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                b_cur[nb] = b_nxt[nb];
-                b_nxt[nb] = b_nn[nb];
-            }
         }
     }
 
-    // Lane (i16, g) of row block mb holds rows d0 + 16 mb + 4 g + e, column
-    // l_base + 16 nb + i16. All reads of the old S are issued before any
-    // write (one round trip instead of one per element); rows past d fall
-    // outside the buffer view, so their loads return zero and their stores
-    // are dropped.
-    float *dst = part ? part + static_cast<size_t>(sp) * D * R : S;
-    const __amdgpu_buffer_rsrc_t s_rs =
-        __builtin_amdgcn_make_buffer_rsrc(dst, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
-    const bool add_old = accumulate && !part;
-    float old[MBW][4][NBW];
+    // Epilogue: the accumulators go through LDS into row-major order, so that
+    // the read-modify-write of S is whole 16-byte chunks of rows. Lane
+    // (i16, g) of row block mb holds rows 16 mb + 4 g + e, column
+    // l_base + 16 nb + i16.
+    lds_barrier();   // every wave is done with the ring
 #pragma unroll
-    for (int j = 0; j < MBW; ++j)
+    for (int j = 0; j < MBW; ++j) {
+        const int mb = wm + j * WM;
+        if (mb < nmb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+            for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int mb = wm + j * WM;
-                const int i = d0 + 16 * mb + 4 * g + e;
-                const uint32_t off = (mb < nmb && add_old)
-                                         ? static_cast<uint32_t>((i * R + l_base + 16 * nb + i16) * 4)
-                                         : kOob;
-                old[j][e][nb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s_rs, off, 0, 0));
-            }
+                for (int e = 0; e < 4; ++e)
+                    tile[(16 * mb + 4 * g + e) * kTileLd + l_base + 16 * nb + i16] = acc[j][nb][e];
+        }
+    }
+    lds_barrier();
 #pragma unroll
-    for (int j = 0; j < MBW; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int mb = wm + j * WM;
-                const int i = d0 + 16 * mb + 4 * g + e;
-                const uint32_t off =
-                    mb < nmb ? static_cast<uint32_t>((i * R + l_base + 16 * nb + i16) * 4) : kOob;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old[j][e][nb] + acc[j][nb][e]), s_rs,
-                                                      off, 0, 0);
-            }
+    for (int c = 0; c < kOutChunks; ++c) {
+        const int q = tid + 256 * c;
+        const int row = min(q / kRowChunks, kTileRows - 1), col = 4 * (q % kRowChunks);
+        f32x4_t v = *reinterpret_cast<const f32x4_t *>(&tile[row * kTileLd + col]);
+        if (add_old) v += __builtin_bit_cast(f32x4_t, old[c]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), s_rs, out_off(c), 0, 0);
+    }
 }
 
 // S = [S +] (part_0 + part_1 + ...), token splits added in order.

@@ -7,17 +7,13 @@
 
 namespace logra {
 
-// Work split of the first sketch product P = X A^T (bf16 path): row tiles of
-// tile_m tokens times `ks` chunks of k, each chunk kchunk columns (a multiple
-// of 64). Partial sums live in the workspace, followed by P in bf16.
+// Work split of the first sketch product P = X A^T (bf16 path): one
+// workgroup per 32 tokens and 128-column (or r-column) tile of the signs.
+// P (bf16, t_blocks x r x 32) is the first thing in the sketch workspace.
 struct Stage1Plan {
-    int tile_m = 0;
-    int n_mtiles = 0;
-    int ks = 0;
-    int kchunk = 0;
-    int64_t t_pad = 0;        // n_mtiles * tile_m
-    size_t part_bytes = 0;    // ks * t_pad * r * 4
-    size_t p_bytes = 0;       // t_pad * r * 2
+    int t_blocks = 0;         // 32-token blocks
+    int col_tiles = 0;
+    size_t p_bytes = 0;       // t_blocks * 32 * r * 2
 };
 
 Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R);

@@ -7,177 +7,184 @@
 // Sketches", paragraph "Gradient sketches."). Two products, both dense
 // contractions on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation:
 //
-//   stage 1   P = c * X Sigma^T  (T x r, contraction over k). A's sign tiles
-//             are made in registers from the counter hash: one 64-bit word per
-//             lane per 64 columns, shuffled to the lanes of each 16-column
-//             block, bytes expanded to bf16 +-1. The k range is split across
-//             workgroups so that a microbatch fills the GPU; partial sums go to
-//             the workspace and a finalize pass adds them in a fixed order,
-//             scales by c and rounds P to bf16 (nearest even) in a layout whose
-//             16-byte chunks are exactly the stage-2 operand fragments.
+//   stage 1   P = c * X Sigma^T  (T x r, contraction over k), this file.
 //   stage 2   S (+)= dY^T P  (d x r, contraction over the tokens): the fold
 //             kernel in fold_bf16.hip.
+//
+// Stage 1 design. A workgroup owns 32 tokens x 128 (or r, if smaller) sign
+// columns over the whole of k, so no partial sums leave the chip: its eight
+// waves (two per SIMD, so one wave's sign arithmetic overlaps the other's
+// matrix and memory work) split the k range, each accumulating the full
+// 32 x 128 tile, and add their tiles through LDS in a fixed order at the end.
+// Sigma is never stored: each wave hashes the 64-bit sign words of its k range
+// into an LDS table (8 word blocks at a time), and every step expands one byte per lane into
+// eight bf16 +-1 values, the B operand of the MFMA. X streams straight from
+// HBM through buffer loads (rows past T and columns past k read as zero)
+// several steps ahead of use. The result is scaled by c, rounded to bf16
+// (nearest even) and written in the fold's operand layout
+// P[t / 32][l][t % 32], so a 16-byte load there is one MFMA fragment.
 #include "common.hpp"
 #include "launch.hpp"
 #include "signs.hpp"
 
 namespace logra {
 
+constexpr int kS1Tokens = 32;     // tokens per workgroup (two 16-row MFMA blocks)
+constexpr int kS1Waves = 8;       // waves per workgroup; they split the k range
+constexpr int kS1Words = 8;       // sign-word blocks (64 columns of k each) hashed per refill
+constexpr int kS1Prefetch = 8;    // steps of X held in registers ahead of use
+constexpr int kS1TileLd = 36;     // fp32 stride of one column of the reduction tile (32 + 4)
+
 template <int R>
-struct SketchShape {
-    static constexpr int NB = R / 16;            // 16-wide column blocks of r
-    static constexpr int WN = NB < 4 ? NB : 4;   // waves across r
-    static constexpr int NBW = NB / WN;          // column blocks per wave
-    static constexpr int WM = 4 / WN;            // waves across rows
+struct Stage1Shape {
+    static constexpr int RT = R < 128 ? R : 128;   // sign columns per workgroup
+    static constexpr int NB = RT / 16;             // 16-column MFMA blocks per wave
+    static constexpr int NCT = R / RT;             // column tiles
     static_assert(R % 32 == 0 && R <= 256, "bf16 sketch supports r in {32,64,128,256}");
 };
 
-constexpr int kS1RowBlocks = 8;   // 16-row MFMA blocks per wave in stage 1 (128 tokens)
-
 // ---------------------------------------------------------------- stage 1 --
 template <int R>
-__global__ __launch_bounds__(256) void stage1_bf16_kernel(
-    const uint16_t *__restrict__ X, int64_t ldx, int T, int K, uint64_t key, int kchunk,
-    float *__restrict__ part, int t_pad) {
-    using Sh = SketchShape<R>;
-    constexpr int MBW = kS1RowBlocks;
-    constexpr int NBW = Sh::NBW;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave / Sh::WN, wn = wave % Sh::WN;
-    const int n = lane & 15, g = lane >> 4;
-    const int t_base = blockIdx.x * (Sh::WM * 128) + wm * 128;
-    const int l_base = wn * NBW * 16;
-    const int split = blockIdx.y;
-    const int j_begin = split * kchunk;
-    const int j_end = min(K, j_begin + kchunk);
+__global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx,
+                                                          int T, int K, uint64_t key, float c,
+                                                          uint16_t *__restrict__ P) {
+    using Sh = Stage1Shape<R>;
+    constexpr int RT = Sh::RT, NB = Sh::NB, PF = kS1Prefetch;
+    constexpr int kTableBytes = kS1Waves * kS1Words * RT * 8;
+    constexpr int kTileBytes = kS1Waves * RT * kS1TileLd * 4;
+    // The per-wave sign-word tables during the loop, the reduction tile after it.
+    __shared__ __attribute__((aligned(16))) char smem[kTableBytes > kTileBytes ? kTableBytes : kTileBytes];
+    uint64_t *table = reinterpret_cast<uint64_t *>(smem);
+    float *tile = reinterpret_cast<float *>(smem);
 
-    f32x4_t acc[MBW][NBW];
-#pragma unroll
-    for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero_f32x4();
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i16 = lane & 15, g = lane >> 4;
+    const int tb = blockIdx.x;                 // 32-token block
+    const int l0 = blockIdx.y * RT;            // first sign column of the tile
+    const int t0 = tb * kS1Tokens;
 
-    const uint16_t *xrow[MBW];
-    bool rowok[MBW];
+    // This wave's share of k, in whole 64-column word blocks.
+    const int nkb = (K + 63) >> 6;
+    const int bpw = (nkb + kS1Waves - 1) / kS1Waves;
+    const int kb0 = min(nkb, wave * bpw), kb1 = min(nkb, kb0 + bpw);
+    const int s_begin = 2 * kb0;
+    const int s_end = min((K + 31) >> 5, 2 * kb1);   // 32-column steps
+
+    // X fragments: lane (i16, g) of row block mb holds X[t0 + 16 mb + i16][32 s + 8 g .. +7].
+    constexpr uint32_t kOob = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(X), 0, static_cast<int>(static_cast<int64_t>(T) * ldx * 2), 0x00020000);
+    uint32_t row_off[2];
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-        const int t = t_base + 16 * mb + n;
-        rowok[mb] = t < T;
-        xrow[mb] = X + static_cast<int64_t>(rowok[mb] ? t : 0) * ldx;
+    for (int mb = 0; mb < 2; ++mb) {
+        const int t = t0 + 16 * mb + i16;
+        row_off[mb] = t < T ? static_cast<uint32_t>(static_cast<int64_t>(t) * ldx * 2) : kOob;
     }
+    auto xload = [&](int s, int mb) -> u32x4_t {
+        const int k = 32 * s + 8 * g;
+        const uint32_t off = (row_off[mb] != kOob && s < s_end && k < K) ? row_off[mb] + 2u * k : kOob;
+        return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0));
+    };
 
-    const int s_begin = j_begin >> 5;           // 32-column steps; j_begin % 64 == 0
-    const int s_end = (j_end + 31) >> 5;
-
-    u32x4_t a_cur[MBW];
-    {
-        const int jj = (s_begin << 5) + 8 * g;
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-            a_cur[mb] = (rowok[mb] && jj < j_end) ? load_u32x4(xrow[mb] + jj) : zero_u32x4();
-    }
-    uint32_t wlo[NBW], whi[NBW];
-    const uint32_t my_l = static_cast<uint32_t>(l_base + (lane % (NBW * 16)));
-
-    for (int s = s_begin; s < s_end; ++s) {
-        u32x4_t a_nxt[MBW];
-        if (s + 1 < s_end) {
-            const int jj = ((s + 1) << 5) + 8 * g;
-#pragma unroll
-            for (int mb = 0; mb < MBW; ++mb)
-                a_nxt[mb] = (rowok[mb] && jj < j_end) ? load_u32x4(xrow[mb] + jj) : zero_u32x4();
+    // Sign words of this wave's k range, kS1Words blocks at a time:
+    // table[wave][block - first][column].
+    uint64_t *wt = table + wave * (kS1Words * RT);
+    auto refill = [&](int first) {
+        for (int idx = lane; idx < kS1Words * RT; idx += 64) {
+            const int bb = idx / RT, col = idx - bb * RT;
+            const int b = first + bb;
+            wt[idx] = b < kb1 ? sign_word(key, static_cast<uint32_t>(l0 + col), static_cast<uint32_t>(b)) : 0ull;
         }
-        if (((s - s_begin) & 1) == 0) {
-            // one sign word per lane: row my_l, columns 64*(s/2) .. +63
-            const uint64_t w = sign_word(key, my_l, static_cast<uint32_t>(s >> 1));
-            const int lo = static_cast<int>(static_cast<uint32_t>(w));
-            const int hi = static_cast<int>(static_cast<uint32_t>(w >> 32));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    };
+
+    f32x4_t acc[2][NB];
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int src = nb * 16 + n;
-                wlo[nb] = static_cast<uint32_t>(__shfl(lo, src, 64));
-                whi[nb] = static_cast<uint32_t>(__shfl(hi, src, 64));
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero_f32x4();
+
+    u32x4_t xa[PF][2];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) xa[p][mb] = xload(s_begin + p, mb);
+
+    int first = kb0;   // first block held in the table
+    if (s_begin < s_end) refill(first);
+    // Whole groups of PF steps; steps past s_end load zeros and their
+    // (zero) products are skipped.
+    for (int s0 = s_begin; s0 < s_end; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int s = s0 + p;
+            if (s < s_end) {
+                const int b = s >> 1;
+                if (b >= first + kS1Words) {
+                    first += kS1Words;
+                    refill(first);
+                }
+                // B fragments: columns 16 nb + i16, k = 32 s + 8 g .. +7, i.e.
+                // byte 4 (s & 1) + g of the word.
+                u32x4_t bf[NB];
+                const uint64_t *wrow = wt + (b - first) * RT + i16;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint64_t w = wrow[16 * nb];
+                    const uint32_t dw = (s & 1) ? static_cast<uint32_t>(w >> 32) : static_cast<uint32_t>(w);
+                    bf[nb] = signs8_to_bf16(__builtin_amdgcn_ubfe(dw, 8 * g, 8));
+                }
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_bf16(xa[p][mb], bf[nb], acc[mb][nb]);
             }
-        }
-        u32x4_t bfrag[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const uint32_t dw = (s & 1) ? whi[nb] : wlo[nb];
-            bfrag[nb] = signs8_to_bf16((dw >> (8 * g)) & 0xFFu);
-        }
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma_bf16(a_cur[mb], bfrag[nb], acc[mb][nb]);
-        if (s + 1 < s_end) {
-#pragma unroll
-            for (int mb = 0; mb < MBW; ++mb) a_cur[mb] = a_nxt[mb];
+            for (int mb = 0; mb < 2; ++mb) xa[p][mb] = xload(s + PF, mb);
         }
     }
 
-    // partial tile -> part[split][t/32][l][t%32] (fp32, 4 consecutive tokens per lane)
-    const size_t tb_count = static_cast<size_t>(t_pad >> 5);
+    // The waves' tiles go to LDS as tile[wave][column][token] and are added
+    // in wave order. Lane (i16, g) of block (mb, nb) holds tokens
+    // 16 mb + 4 g .. +3 of column 16 nb + i16.
+    __syncthreads();   // every wave is done with its word table
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-        const int t = t_base + 16 * mb + 4 * g;
-        const size_t tb = static_cast<size_t>(t >> 5);
-        const int tt = t & 31;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const int l = l_base + 16 * nb + n;
-            float *dst = part + ((static_cast<size_t>(split) * tb_count + tb) * R + l) * 32 + tt;
-            *reinterpret_cast<f32x4_t *>(dst) = acc[mb][nb];
+        for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<f32x4_t *>(&tile[(wave * RT + 16 * nb + i16) * kS1TileLd + 16 * mb + 4 * g]) =
+                acc[mb][nb];
+    __syncthreads();
+    // Output chunks: column q / 4, tokens 8 (q % 4) .. +7 (16 bytes of P).
+    for (int q = tid; q < RT * 4; q += 64 * kS1Waves) {
+        const int col = q >> 2, tq = 8 * (q & 3);
+        f32x4_t lo = zero_f32x4(), hi = zero_f32x4();
+#pragma unroll
+        for (int w = 0; w < kS1Waves; ++w) {
+            const float *src = &tile[(w * RT + col) * kS1TileLd + tq];
+            lo += *reinterpret_cast<const f32x4_t *>(src);
+            hi += *reinterpret_cast<const f32x4_t *>(src + 4);
         }
+        u32x4_t o;
+        o.x = pack_bf16x2(c * lo.x, c * lo.y);
+        o.y = pack_bf16x2(c * lo.z, c * lo.w);
+        o.z = pack_bf16x2(c * hi.x, c * hi.y);
+        o.w = pack_bf16x2(c * hi.z, c * hi.w);
+        *reinterpret_cast<u32x4_t *>(P + (static_cast<size_t>(tb) * R + l0 + col) * 32 + tq) = o;
     }
-}
-
-// P[t/32][l][t%32] = bf16(c * sum over splits of the partials), splits added in order.
-template <int R>
-__global__ __launch_bounds__(256) void stage1_finalize_kernel(const float *__restrict__ part, int ks,
-                                                              int t_pad, float c,
-                                                              uint16_t *__restrict__ P) {
-    const size_t total = static_cast<size_t>(t_pad >> 5) * R * 4;   // 8 tokens per thread
-    const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    const size_t base = idx * 8;
-    const size_t slab = static_cast<size_t>(t_pad) * R;
-    f32x4_t s0 = zero_f32x4(), s1 = zero_f32x4();
-    for (int sp = 0; sp < ks; ++sp) {
-        const float *p = part + sp * slab + base;
-        s0 += *reinterpret_cast<const f32x4_t *>(p);
-        s1 += *reinterpret_cast<const f32x4_t *>(p + 4);
-    }
-    u32x4_t o;
-    o.x = pack_bf16x2(c * s0.x, c * s0.y);
-    o.y = pack_bf16x2(c * s0.z, c * s0.w);
-    o.z = pack_bf16x2(c * s1.x, c * s1.y);
-    o.w = pack_bf16x2(c * s1.z, c * s1.w);
-    *reinterpret_cast<u32x4_t *>(P + base) = o;
 }
 
 // ----------------------------------------------------------------- plans --
-static int stage1_tile_m(int R) {
-    const int nb = R / 16;
-    const int wn = nb < 4 ? nb : 4;
-    return (4 / wn) * 128;
-}
-
 Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R) {
     Stage1Plan p;
+    (void)K;
     if (T <= 0) return p;
-    p.tile_m = stage1_tile_m(R);
-    p.n_mtiles = static_cast<int>((T + p.tile_m - 1) / p.tile_m);
-    const int nkb = static_cast<int>((K + 63) / 64);
-    const int target = 512;   // about two workgroups per compute unit
-    int ks = (target + p.n_mtiles - 1) / p.n_mtiles;
-    if (ks < 1) ks = 1;
-    if (ks > nkb) ks = nkb;
-    const int blocks_per = (nkb + ks - 1) / ks;
-    p.ks = (nkb + blocks_per - 1) / blocks_per;
-    p.kchunk = blocks_per * 64;
-    p.t_pad = static_cast<int64_t>(p.n_mtiles) * p.tile_m;
-    p.part_bytes = static_cast<size_t>(p.ks) * p.t_pad * R * 4;
-    p.p_bytes = static_cast<size_t>(p.t_pad) * R * 2;
+    p.t_blocks = static_cast<int>((T + kS1Tokens - 1) / kS1Tokens);
+    p.col_tiles = R / (R < 128 ? R : 128);
+    p.p_bytes = static_cast<size_t>(p.t_blocks) * kS1Tokens * R * 2;
     return p;
 }
 
@@ -185,14 +192,9 @@ template <int R>
 static hipError_t project_bf16_r(int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
                                  int64_t ldx, void *ws, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
-    float *part = static_cast<float *>(ws);
-    uint16_t *P = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + p.part_bytes);
-    hipLaunchKernelGGL(stage1_bf16_kernel<R>, dim3(p.n_mtiles, p.ks), dim3(256), 0, st, X, ldx,
-                       static_cast<int>(T), static_cast<int>(K), key, p.kchunk, part,
-                       static_cast<int>(p.t_pad));
-    const size_t fin_threads = static_cast<size_t>(p.t_pad / 32) * R * 4;
-    hipLaunchKernelGGL(stage1_finalize_kernel<R>, dim3((fin_threads + 255) / 256), dim3(256), 0, st,
-                       part, p.ks, static_cast<int>(p.t_pad), c, P);
+    uint16_t *P = static_cast<uint16_t *>(ws);
+    hipLaunchKernelGGL(stage1_bf16_kernel<R>, dim3(p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
+                       static_cast<int>(T), static_cast<int>(K), key, c, P);
     return hipGetLastError();
 }
 
@@ -201,10 +203,9 @@ static hipError_t fold_bf16_r(int64_t T, int64_t D, int64_t K, const uint16_t *d
                               float *S, int accumulate, const void *ws, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
     const char *base = static_cast<const char *>(ws);
-    const uint16_t *P = reinterpret_cast<const uint16_t *>(base + p.part_bytes);
-    float *part = reinterpret_cast<float *>(const_cast<char *>(base) + p.part_bytes + p.p_bytes);
-    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, static_cast<int>(p.t_pad / 32), S, accumulate,
-                                  part, st);
+    const uint16_t *P = reinterpret_cast<const uint16_t *>(base);
+    float *part = reinterpret_cast<float *>(const_cast<char *>(base) + p.p_bytes);
+    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, p.t_blocks, S, accumulate, part, st);
 }
 
 hipError_t launch_project_bf16(int R, int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,

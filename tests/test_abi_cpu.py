@@ -98,8 +98,11 @@ def test_workspace_sizes(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
     m = B.MatrixDesc(18944, 3584, 256)
     ws = B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_BF16)
-    # split partials (fp32) + the projected microbatch (bf16), both T x r
-    assert ws >= 4096 * 256 * (4 + 2) and ws % 16 == 0
+    # the projected microbatch X A^T in bf16 (T x r); this d needs no split of the fold
+    assert ws == 4096 * 256 * 2
+    # a small d splits the fold over tokens: fp32 partial tiles follow P
+    small = B.logra_sketch_workspace_bytes(B.MatrixDesc(512, 3584, 256), 4096, B.LOGRA_BF16)
+    assert small > 4096 * 256 * 2 and (small - 4096 * 256 * 2) % (512 * 256 * 4) == 0
     assert B.logra_sketch_workspace_bytes(m, 0, B.LOGRA_BF16) == 0
     assert B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_F32) == 4096 * 256 * 4
     assert B.logra_sketch_workspace_bytes(B.MatrixDesc(64, 64, 48), 16, B.LOGRA_BF16) == 0
