@@ -6,19 +6,27 @@
 // "Why it matters"); RowAdam keeps one running second moment per row and no
 // first moment (same page, "What happened" and "Why it matters").
 //
-// Layout: a workgroup (4 waves) owns 64 rows of W and a range of 128-column
-// tiles; the grid is (row tiles) x (column ranges) so that every CU gets
-// several workgroups. The MFMA computes Ghat^T tiles: A operand = sign
-// fragments (16 columns j x 32 rank indices l), B operand = S^T (32 l x 16
-// rows i; S rounded to bf16 once per workgroup and kept in registers), so each
-// lane's accumulator holds consecutive columns of one row of W and W moves in
-// 16-byte vectors. MFMA row m of column block mb stands for column
-// 8*(m/4) + 4*mb + m%4 of the wave's 32, which puts columns 8g .. 8g+7 of row
-// i in lane (i, g). The sign words of the current 128 columns (2 x r words)
-// are hashed into LDS once per workgroup and tile. W goes through a buffer
-// view (rows past d and columns past k read as zero and are not written), and
-// the next tile's W is requested before the current tile's products, so the
-// W stream overlaps the matrix work instead of waiting on it.
+// Work decomposition. The unit of work is one 256-row tile of W times one
+// 64-column tile; the units, in row-major order, are dealt to a fixed number
+// of workgroups as contiguous, equally sized ranges (one workgroup per
+// compute unit), so a workgroup touches at most a few row tiles and loads
+// their rows of S only once each. Neighbouring ranges (which share a row
+// tile) run on the same XCD, so S is fetched from HBM about once and the
+// other workgroups of the row tile find it in that XCD's L2. Eight waves
+// (two per SIMD, so one wave's vector work overlaps the other's matrix work)
+// each own 32 of the 256 rows and keep S^T for them as bf16 MFMA operands in
+// registers.
+//
+// Per column tile: every thread hashes one 64-bit sign word (rank row l,
+// these 64 columns) into LDS; each wave then builds an eighth of the tile's
+// 32 sign fragments (16 columns x 32 rank indices, bf16 +-1) from the words
+// and stores them to LDS, so every fragment is built once per workgroup and
+// read by all eight waves. The MFMA computes Ghat^T tiles (A = signs, B =
+// S^T); MFMA row m of pseudo column block cb stands for column
+// 32 (cb / 2) + 8 (m / 4) + 4 (cb % 2) + m % 4, which puts 8 consecutive
+// columns of one row of W in each lane, so W moves in 16-byte vectors. W
+// goes through a buffer view (rows past d and columns past k read as zero
+// and are not written) and is requested two tiles ahead of its update.
 //
 // Every workgroup of a row tile reads v and rowsq to form u_i; v itself is
 // committed by a separate small pass once all of them are done.
@@ -29,139 +37,251 @@
 namespace logra {
 
 constexpr uint32_t kOobOff = 0x80000000u;
+constexpr int kApplyRows = 256;        // rows of W per row tile (32 per wave)
+constexpr int kApplyWaves = 8;
+constexpr int kApplyCols = 64;         // columns per column tile (one sign word)
+constexpr int kApplyWGs = 256;         // workgroups (one per compute unit)
+
+// Barrier that orders LDS traffic only (global loads stay in flight).
+__device__ __forceinline__ void apply_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int R, bool WBF16>
-__global__ __launch_bounds__(256) void rowadam_bf16_kernel(ApplyArgs a, int it_per) {
+__global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct, int n_units) {
     constexpr int KS = R / 32;                 // 32-wide steps of the rank
     constexpr int WV = WBF16 ? 1 : 2;          // 16-byte vectors per 8 columns of W
-    __shared__ uint32_t words[2][2][2][R];     // [buffer][column block][half][l]
-    __shared__ float coef_s[64];
+    constexpr int NF = 4 * KS;                 // sign fragments per column tile
+    __shared__ uint32_t words[2][2][R];        // [buffer][half of the 64 columns][l]
+    __shared__ __attribute__((aligned(16))) u32x4_t frags[2][NF][64];   // [buffer][fragment][lane]
+    __shared__ float coef_s[kApplyRows];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int D = static_cast<int>(a.D), K = static_cast<int>(a.K);
-    const int i_base = blockIdx.x * 64;
-    const int niter = (K + 127) / 128;
-    const int it_begin = blockIdx.y * it_per;
-    const int it_end = min(niter, it_begin + it_per);
 
-    // S^T fragments: lane (n, g) of block nb, step s holds S[i][32s + 8g .. +7], i = i_base+16nb+n
-    u32x4_t sf[4][KS];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int i = min(i_base + 16 * nb + n, D - 1);   // rows past d compute junk, never stored
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const float *p = a.S + static_cast<int64_t>(i) * R + 32 * s + 8 * g;
-            const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(p);
-            const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(p + 4);
-            sf[nb][s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                                pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
-        }
-    }
-    if (tid < 64) {
-        const int i = i_base + tid;
-        float coef = 0.f;
-        if (i < D) {
-            const float vn = a.beta2 * a.v[i] + (1.f - a.beta2) * (a.rowsq_in[i] / static_cast<float>(K));
-            coef = a.lr_scale * a.c / (sqrtf(vn) + a.eps);
-        }
-        coef_s[tid] = coef;
-    }
+    // workgroup ids are dealt round-robin over the 8 XCDs
+    const int G = gridDim.x;
+    const int range = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : static_cast<int>(blockIdx.x);
+    const int u_begin = static_cast<int>((static_cast<int64_t>(range) * n_units) / G);
+    const int u_end = static_cast<int>((static_cast<int64_t>(range + 1) * n_units) / G);
 
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.W, 0, static_cast<int>(static_cast<int64_t>(D) * a.ldw * (WBF16 ? 2 : 4)), 0x00020000);
-    // byte offset of this lane's 8 columns in row block nb, tile it (kOobOff if masked)
-    auto w_off = [&](int it, int nb) -> uint32_t {
-        const int i = i_base + 16 * nb + n;
-        const int jc = it * 128 + 32 * wave + 8 * g;
-        const bool ok = it < it_end && i < D && jc < K;
-        return ok ? static_cast<uint32_t>((static_cast<int64_t>(i) * a.ldw + jc) * (WBF16 ? 2 : 4))
-                  : kOobOff;
+    // Position of a unit: row tile, column tile (advanced one unit at a time).
+    struct Pos {
+        int u, rt, ct;
     };
-    auto w_load = [&](int it, u32x4_t (&w)[4][WV]) {
+    auto advance = [&](Pos p) -> Pos {
+        ++p.u;
+        if (++p.ct == n_ct) {
+            p.ct = 0;
+            ++p.rt;
+        }
+        return p;
+    };
+    // Byte offset of lane (n, g)'s 8 columns of row block rb, column half h,
+    // in unit p (kOobOff if masked).
+    auto w_off = [&](const Pos &p, int rb, int h) -> uint32_t {
+        const int i = p.rt * kApplyRows + 32 * wave + 16 * rb + n;
+        const int jc = p.ct * kApplyCols + 32 * h + 8 * g;
+        const bool ok = p.u < u_end && i < D && jc < K;
+        return ok ? static_cast<uint32_t>((static_cast<int64_t>(i) * a.ldw + jc) * (WBF16 ? 2 : 4)) : kOobOff;
+    };
+    auto w_load = [&](const Pos &p, u32x4_t (&w)[2][2][WV]) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const uint32_t off = w_off(it, nb);
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int h = 0; h < WV; ++h)
-                w[nb][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           w_rs, off == kOobOff ? off : off + 16 * h, 0, 0));
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t off = w_off(p, rb, h);
+#pragma unroll
+                for (int x = 0; x < WV; ++x)
+                    w[rb][h][x] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  w_rs, off == kOobOff ? off : off + 16 * x, 0, 0));
+            }
+    };
+    // Sign words of unit p: thread l (< R) hashes rank row l, word block ct.
+    auto hash_words = [&](const Pos &p, int buf) {
+        if (tid < R && p.u < u_end) {
+            const uint64_t w = sign_word(a.key, static_cast<uint32_t>(tid), static_cast<uint32_t>(p.ct));
+            words[buf][0][tid] = static_cast<uint32_t>(w);
+            words[buf][1][tid] = static_cast<uint32_t>(w >> 32);
         }
     };
-
-    // bit of column (j0 + 32*wave + jmap(mb, n)) inside the wave's 32-bit half word
+    // Fragment (cb, s), lane (n, g): rank rows l = 32 s + 8 g + e (e = 0..7),
+    // column 32 (cb / 2) + 8 (n / 4) + 4 (cb % 2) + n % 4; element e is
+    // +-1 in bf16, element pairs packed low half first. Wave w builds the
+    // fragments of steps s with s % 8 == w.
     const int jbit = 8 * (n >> 2) + (n & 3);
-    const int b2 = wave >> 1, half = wave & 1;
-
-    u32x4_t wcur[4][WV], wnxt[4][WV];
-    w_load(it_begin, wcur);
-    for (int it = it_begin; it < it_end; ++it) {
-        const int j0 = it * 128;
-        const int buf = it & 1;
-        for (int idx = tid; idx < 2 * R; idx += 256) {
-            const int bb = idx / R, l = idx - bb * R;
-            const uint64_t w = sign_word(a.key, static_cast<uint32_t>(l),
-                                         static_cast<uint32_t>((j0 >> 6) + bb));
-            words[buf][bb][0][l] = static_cast<uint32_t>(w);
-            words[buf][bb][1][l] = static_cast<uint32_t>(w >> 32);
-        }
-        w_load(it + 1, wnxt);   // next tile's W in flight during this tile's products
-        __syncthreads();
-        const uint32_t *wp = &words[buf][b2][half][0];
-        f32x4_t acc[2][4];
+    auto build_step = [&](int buf, int s) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero_f32x4();
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            // words of rank rows l = 32s + 8g .. +7 (same for all 16 lanes of a group)
-            const u32x4_t w0 = *reinterpret_cast<const u32x4_t *>(wp + 32 * s + 8 * g);
-            const u32x4_t w1 = *reinterpret_cast<const u32x4_t *>(wp + 32 * s + 8 * g + 4);
+        for (int h = 0; h < 2; ++h) {
+            const u32x4_t w0 = *reinterpret_cast<const u32x4_t *>(&words[buf][h][32 * s + 8 * g]);
+            const u32x4_t w1 = *reinterpret_cast<const u32x4_t *>(&words[buf][h][32 * s + 8 * g + 4]);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const int sh = jbit + 4 * mb;
-                u32x4_t af;
-                af.x = 0x3F803F80u | (((w0.x >> sh) & 1u) << 15) | (((w0.y >> sh) & 1u) << 31);
-                af.y = 0x3F803F80u | (((w0.z >> sh) & 1u) << 15) | (((w0.w >> sh) & 1u) << 31);
-                af.z = 0x3F803F80u | (((w1.x >> sh) & 1u) << 15) | (((w1.y >> sh) & 1u) << 31);
-                af.w = 0x3F803F80u | (((w1.z >> sh) & 1u) << 15) | (((w1.w >> sh) & 1u) << 31);
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(af, sf[nb][s], acc[mb][nb]);
+                const uint32_t sh = jbit + 4 * mb;
+                u32x4_t f;
+                f.x = __builtin_amdgcn_ubfe(w0.y, sh, 1) << 31 | __builtin_amdgcn_ubfe(w0.x, sh, 1) << 15 | 0x3F803F80u;
+                f.y = __builtin_amdgcn_ubfe(w0.w, sh, 1) << 31 | __builtin_amdgcn_ubfe(w0.z, sh, 1) << 15 | 0x3F803F80u;
+                f.z = __builtin_amdgcn_ubfe(w1.y, sh, 1) << 31 | __builtin_amdgcn_ubfe(w1.x, sh, 1) << 15 | 0x3F803F80u;
+                f.w = __builtin_amdgcn_ubfe(w1.w, sh, 1) << 31 | __builtin_amdgcn_ubfe(w1.z, sh, 1) << 15 | 0x3F803F80u;
+                frags[buf][(2 * h + mb) * KS + s][lane] = f;
             }
         }
-        // lane (n, g) of block nb holds Ghat/c for row i_base+16nb+n, columns
-        // jc .. jc+7 (acc[0] the first four, acc[1] the next four)
+    };
+    auto build_frags = [&](int buf) {
+        if constexpr (KS % kApplyWaves == 0) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const float cf = coef_s[16 * nb + n];
-            const f32x4_t x0 = acc[0][nb], x1 = acc[1][nb];
-            const uint32_t off = w_off(it, nb);
-            if (WBF16) {
-                const u32x4_t wv = wcur[nb][0];
-                u32x4_t o;
-                o.x = pack_bf16x2(fmaf(-cf, x0.x, bf16_lo(wv.x)), fmaf(-cf, x0.y, bf16_hi(wv.x)));
-                o.y = pack_bf16x2(fmaf(-cf, x0.z, bf16_lo(wv.y)), fmaf(-cf, x0.w, bf16_hi(wv.y)));
-                o.z = pack_bf16x2(fmaf(-cf, x1.x, bf16_lo(wv.z)), fmaf(-cf, x1.y, bf16_hi(wv.z)));
-                o.w = pack_bf16x2(fmaf(-cf, x1.z, bf16_lo(wv.w)), fmaf(-cf, x1.w, bf16_hi(wv.w)));
-                __builtin_amdgcn_raw_buffer_store_b128(o, w_rs, off, 0, 0);
-            } else {
-                f32x4_t w0v = __builtin_bit_cast(f32x4_t, wcur[nb][0]);
-                f32x4_t w1v = __builtin_bit_cast(f32x4_t, wcur[nb][WV - 1]);
-                w0v.x = fmaf(-cf, x0.x, w0v.x); w0v.y = fmaf(-cf, x0.y, w0v.y);
-                w0v.z = fmaf(-cf, x0.z, w0v.z); w0v.w = fmaf(-cf, x0.w, w0v.w);
-                w1v.x = fmaf(-cf, x1.x, w1v.x); w1v.y = fmaf(-cf, x1.y, w1v.y);
-                w1v.z = fmaf(-cf, x1.z, w1v.z); w1v.w = fmaf(-cf, x1.w, w1v.w);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w0v), w_rs, off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w1v), w_rs,
-                                                      off == kOobOff ? off : off + 16, 0, 0);
+            for (int j = 0; j < KS / kApplyWaves; ++j) build_step(buf, wave + kApplyWaves * j);
+        } else {
+            for (int s = wave; s < KS; s += kApplyWaves) build_step(buf, s);
+        }
+    };
+
+    // S^T fragments of the current row tile: lane (n, g) of row block rb,
+    // step s holds S[i][32 s + 8 g .. +7] in bf16, i = row 32 wave + 16 rb + n
+    // of the tile (rows past d are clamped: their products are never stored).
+    u32x4_t sf[2][KS];
+    int cur_rt = -1;
+    auto load_rows = [&](int rt) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int i = min(rt * kApplyRows + 32 * wave + 16 * rb + n, D - 1);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const float *p = a.S + static_cast<int64_t>(i) * R + 32 * s + 8 * g;
+                const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(p);
+                const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(p + 4);
+                sf[rb][s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                                    pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
             }
         }
+        // u_i for the 256 rows, with the c of A folded in
+        if (tid < kApplyRows) {
+            const int i = rt * kApplyRows + tid;
+            float coef = 0.f;
+            if (i < D) {
+                const float vn = a.beta2 * a.v[i] + (1.f - a.beta2) * (a.rowsq_in[i] / static_cast<float>(K));
+                coef = a.lr_scale * a.c / (sqrtf(vn) + a.eps);
+            }
+            coef_s[tid] = coef;
+        }
+        cur_rt = rt;
+    };
+
+    // W_ij -= cf_i * (Ghat/c)_ij for the unit at p: lane (n, g) of (rb, cb)
+    // holds row 32 wave + 16 rb + n, columns 32 (cb / 2) + 8 g + 4 (cb % 2) .. +3.
+    auto finish = [&](const f32x4_t (&acc)[2][4], const float (&cf)[2], const Pos &p,
+                      const u32x4_t (&wv)[2][2][WV]) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int h = 0; h < WV; ++h) wcur[nb][h] = wnxt[nb][h];
+            for (int h = 0; h < 2; ++h) {
+                const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
+                const uint32_t off = w_off(p, rb, h);
+                const float c = cf[rb];
+                if (WBF16) {
+                    const u32x4_t w = wv[rb][h][0];
+                    u32x4_t o;
+                    o.x = pack_bf16x2(fmaf(-c, x0.x, bf16_lo(w.x)), fmaf(-c, x0.y, bf16_hi(w.x)));
+                    o.y = pack_bf16x2(fmaf(-c, x0.z, bf16_lo(w.y)), fmaf(-c, x0.w, bf16_hi(w.y)));
+                    o.z = pack_bf16x2(fmaf(-c, x1.x, bf16_lo(w.z)), fmaf(-c, x1.y, bf16_hi(w.z)));
+                    o.w = pack_bf16x2(fmaf(-c, x1.z, bf16_lo(w.w)), fmaf(-c, x1.w, bf16_hi(w.w)));
+                    __builtin_amdgcn_raw_buffer_store_b128(o, w_rs, off, 0, 0);
+                } else {
+                    f32x4_t w0v = __builtin_bit_cast(f32x4_t, wv[rb][h][0]);
+                    f32x4_t w1v = __builtin_bit_cast(f32x4_t, wv[rb][h][WV - 1]);
+                    w0v.x = fmaf(-c, x0.x, w0v.x); w0v.y = fmaf(-c, x0.y, w0v.y);
+                    w0v.z = fmaf(-c, x0.z, w0v.z); w0v.w = fmaf(-c, x0.w, w0v.w);
+                    w1v.x = fmaf(-c, x1.x, w1v.x); w1v.y = fmaf(-c, x1.y, w1v.y);
+                    w1v.z = fmaf(-c, x1.z, w1v.z); w1v.w = fmaf(-c, x1.w, w1v.w);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w0v), w_rs, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w1v), w_rs,
+                                                          off == kOobOff ? off : off + 16, 0, 0);
+                }
+            }
+    };
+
+    if (u_begin >= u_end) return;
+    Pos p0;   // the unit whose products are formed
+    p0.u = u_begin;
+    p0.rt = u_begin / n_ct;
+    p0.ct = u_begin - p0.rt * n_ct;
+    Pos pp = p0;    // the unit whose update is written (one behind p0)
+    pp.u = u_end;   // none yet: w_off masks every access of a unit >= u_end
+    const Pos p1 = advance(p0);
+    Pos p2 = advance(p1);   // the unit whose W and sign words are requested
+    u32x4_t wb[3][2][2][WV];   // W ring: slot (u - u_begin) % 3 holds unit u
+    w_load(p0, wb[0]);
+    w_load(p1, wb[1]);
+    hash_words(p0, 0);
+    apply_lds_barrier();
+    build_frags(0);
+    hash_words(p1, 1);
+    f32x4_t prev[2][4];
+    float cf_prev[2] = {0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) prev[rb][cb] = zero_f32x4();
+
+    // Software pipeline, one unit per step: the products of unit u, the
+    // update of unit u - 1 and the sign fragments of unit u + 1 share one
+    // straight-line block, so the matrix cores and the vector units work at
+    // the same time. Units go in groups of three so the W ring index is a
+    // compile-time constant.
+    for (int u0 = u_begin; u0 < u_end; u0 += 3) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            const int u = u0 + p;
+            if (u < u_end) {
+                const int buf = (u - u_begin) & 1;
+                if (p0.rt != cur_rt) {
+                    // every wave is done with the previous row tile's coef_s
+                    __syncthreads();
+                    load_rows(p0.rt);
+                }
+                apply_lds_barrier();   // fragments of u and words of u + 1 are in LDS
+                f32x4_t acc[2][4];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = zero_f32x4();
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) {
+                        const u32x4_t af = frags[buf][cb * KS + s][lane];
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mfma_bf16(af, sf[rb][s], acc[rb][cb]);
+                    }
+                float cf_cur[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) cf_cur[rb] = coef_s[32 * wave + 16 * rb + n];
+                finish(prev, cf_prev, pp, wb[(p + 2) % 3]);   // unit u - 1 (slot (u - 1) % 3)
+                w_load(p2, wb[(p + 2) % 3]);                 // unit u + 2 into the freed slot
+                build_frags(buf ^ 1);
+                hash_words(p2, buf);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    cf_prev[rb] = cf_cur[rb];
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) prev[rb][cb] = acc[rb][cb];
+                }
+                pp = p0;
+                p0 = advance(p0);
+                p2 = advance(p2);
+            }
+        }
+    }
+    // the last unit's update: slot (u_end - 1 - u_begin) % 3
+    switch ((u_end - 1 - u_begin) % 3) {
+    case 0: finish(prev, cf_prev, pp, wb[0]); break;
+    case 1: finish(prev, cf_prev, pp, wb[1]); break;
+    default: finish(prev, cf_prev, pp, wb[2]); break;
     }
 }
 
@@ -180,19 +300,16 @@ hipError_t launch_commit_v(float *v, const float *rowsq, int64_t D, int64_t K, f
 
 template <int R>
 static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
-    const int row_tiles = static_cast<int>((a.D + 63) / 64);
-    const int niter = static_cast<int>((a.K + 127) / 128);
-    // about four workgroups per compute unit in total
-    int n_ranges = (1024 + row_tiles - 1) / row_tiles;
-    if (n_ranges > niter) n_ranges = niter;
-    if (n_ranges < 1) n_ranges = 1;
-    const int it_per = (niter + n_ranges - 1) / n_ranges;
-    n_ranges = (niter + it_per - 1) / it_per;
-    const dim3 grid(row_tiles, n_ranges), block(256);
+    const int n_rt = static_cast<int>((a.D + kApplyRows - 1) / kApplyRows);
+    const int n_ct = static_cast<int>((a.K + kApplyCols - 1) / kApplyCols);
+    const int n_units = n_rt * n_ct;
+    const int grid = n_units < kApplyWGs ? n_units : kApplyWGs;
     if (a.w_bf16)
-        hipLaunchKernelGGL((rowadam_bf16_kernel<R, true>), grid, block, 0, st, a, it_per);
+        hipLaunchKernelGGL((rowadam_bf16_kernel<R, true>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
+                           n_units);
     else
-        hipLaunchKernelGGL((rowadam_bf16_kernel<R, false>), grid, block, 0, st, a, it_per);
+        hipLaunchKernelGGL((rowadam_bf16_kernel<R, false>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
+                           n_units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_commit_v(a.v, a.rowsq_in, a.D, a.K, a.beta2, st);

@@ -21,11 +21,13 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even: one v_cvt_pk_bf16_f32
+// (built as a two-element vector so both halves convert in one instruction).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-    uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    return a | (b << 16);
+    const bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

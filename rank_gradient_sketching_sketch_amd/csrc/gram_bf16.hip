@@ -21,15 +21,16 @@
 
 namespace logra {
 
-// M_off[l][m] (bf16, row-major r x r, zero diagonal). A workgroup owns a 16 x
-// 16 tile of (l, m); the sign words of its 32 rows are hashed into LDS 64
-// columns-blocks at a time and each thread counts the sign differences of
-// its pair.
+// M_off[l][m] (bf16, row-major r x r, zero diagonal) = k - 2 popcount(sigma_l
+// xor sigma_m). A workgroup owns a 16 x 16 tile of (l, m); the sign words of
+// its 32 rows are hashed into LDS 64 blocks at a time (rows padded by one
+// word so the 16 rows of a column read fall on different banks) and each
+// thread counts the sign differences of its pair.
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
 __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M) {
-    __shared__ uint64_t wl[16][kGramChunk];
-    __shared__ uint64_t wm[16][kGramChunk];
+    __shared__ uint64_t wl[16][kGramChunk + 1];
+    __shared__ uint64_t wm[16][kGramChunk + 1];
     const int tid = threadIdx.x;
     const int l0 = blockIdx.y * 16, m0 = blockIdx.x * 16;
     const int tl = tid >> 4, tm = tid & 15;
@@ -45,8 +46,7 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
             const int row = rem / kGramChunk, bb = rem - row * kGramChunk;
             uint64_t w = 0;
             if (bb < bn) {
-                w = sign_word(key, static_cast<uint32_t>((which ? m0 : l0) + row),
-                              static_cast<uint32_t>(b0 + bb));
+                w = sign_word(key, static_cast<uint32_t>((which ? m0 : l0) + row), static_cast<uint32_t>(b0 + bb));
                 if (b0 + bb == nb - 1) w &= last_mask;   // columns past k do not count
             }
             (which ? wm : wl)[row][bb] = w;
@@ -60,113 +60,114 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
     M[static_cast<size_t>(l) * R + m] = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-// One wave per 32 rows of S (two 16-row blocks), four waves per workgroup.
-// Y (32 x r) = S_bf16 M_off accumulates on the matrix cores one 16-column
-// block at a time; each lane dots its Y entries with the fp32 S entries at the
-// same place and also sums their squares, then the 16 lanes of a row add up.
+// rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
+// owns 128 rows of S, one wave 32 of them (two 16-row blocks i). M_off is
+// copied into LDS once per workgroup by direct global-to-LDS loads (no
+// registers), with the 16-byte chunks of row r stored in the order
+// chunk ^ (r mod 16), so a fragment's 16 rows fall on different banks.
+// The MFMA forms 16 x 16 blocks of Y^T with A = rows of M_off (LDS) and
+// B = S^T (bf16, registers). Row r = 4 q + e of block mb stands for
+// m = 32 (mb / 2) + 8 q + 4 (mb % 2) + e (M_off is symmetric, so any order of
+// m is a valid A operand), which puts in lane (n, g) exactly the Y[i][m] whose
+// S[i][m] it already holds in fp32 for its B fragment: the dot product and
+// the squares need no further loads.
 template <int R>
 __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict__ S, int D, int K,
                                                          const uint16_t *__restrict__ M, float c,
                                                          const float *__restrict__ v, float beta2,
                                                          float eps, float *__restrict__ rowsq,
                                                          float *__restrict__ partials) {
-    constexpr int KS = R / 32;   // 32-wide steps of the rank
-    constexpr int NB = R / 16;   // 16-wide column blocks of Y
+    constexpr int KS = R / 32;                 // 32-wide steps of the rank
+    constexpr int NB = R / 16;                 // 16-row blocks of m
+    constexpr int CPR = R / 8;                 // 16-byte chunks per row of M_off
+    constexpr int SW = CPR < 16 ? CPR : 16;    // chunk swizzle period
+    __shared__ __attribute__((aligned(16))) uint16_t ms[R * R];
     __shared__ float terms[4];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int i0 = blockIdx.x * 128 + wave * 32;
 
-    // A fragments: lane (n, g) of block mb, step s = S[i0 + 16 mb + n][32 s + 8 g .. +7] in bf16
-    u32x4_t af[2][KS];
+    // This lane's S values, issued first: row i0 + 16 ib + n, columns
+    // 32 s + 8 g .. +7 (the B fragment before rounding, and the entries its
+    // Y values meet).
+    f32x4_t raw[2][KS][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int i = i0 + 16 * mb + n;
+    for (int ib = 0; ib < 2; ++ib) {
+        const float *srow = S + static_cast<int64_t>(min(i0 + 16 * ib + n, D - 1)) * R;   // rows past d are dropped
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (i < D) {
-                const float *p = S + static_cast<int64_t>(i) * R + 32 * s + 8 * g;
-                const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(p);
-                const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(p + 4);
-                af[mb][s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                                    pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
-            } else {
-                af[mb][s] = zero_u32x4();
-            }
+            raw[ib][s][0] = *reinterpret_cast<const f32x4_t *>(srow + 32 * s + 8 * g);
+            raw[ib][s][1] = *reinterpret_cast<const f32x4_t *>(srow + 32 * s + 8 * g + 4);
         }
     }
-    // row of Y held by lane (n, g), block mb, element e: i0 + 16 mb + 4 g + e
-    float ydot[2][4], ssq[2][4];
+    // stage M_off: each wave instruction moves 64 chunks; lane i's chunk
+    // lands at LDS chunk position q0 + i (row q / CPR, position q % CPR) and
+    // carries logical chunk position ^ (row mod SW)
+    for (int q0 = wave * 64; q0 < R * CPR; q0 += 256) {
+        const int q = q0 + lane;
+        const int row = q / CPR, pos = q - row * CPR;
+        const int ch = pos ^ (row & (SW - 1));
+        __builtin_amdgcn_global_load_lds(M + static_cast<size_t>(row) * R + 8 * ch,
+                                         (__attribute__((address_space(3))) void *)(ms + q0 * 8), 16, 0, 0);
+    }
+    u32x4_t bt[2][KS];
+    float ssq[2] = {0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ydot[mb][e] = ssq[mb][e] = 0.f;
+        for (int s = 0; s < KS; ++s) {
+            const f32x4_t lo = raw[ib][s][0], hi = raw[ib][s][1];
+            bt[ib][s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
+                                pack_bf16x2(hi.z, hi.w)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ssq[ib] = fmaf(hi[e], hi[e], fmaf(lo[e], lo[e], ssq[ib]));
+        }
+    __syncthreads();
 
-    // B fragments: M_off[32 s + 8 g + e][16 nb + n] = M_off[16 nb + n][32 s + 8 g + e]
-    // (M is symmetric); fetched one column block ahead, with the fp32 S entries
-    auto fetch = [&](int nb, u32x4_t (&bf)[KS], float (&sv)[2][4]) {
+    // A row n of block mb: m = 32 (mb / 2) + 8 (n / 4) + 4 (mb % 2) + n % 4
+    const int mrow_base = 8 * (n >> 2) + (n & 3);
+    float ydot[2] = {0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            bf[s] = load_u32x4(M + static_cast<size_t>(16 * nb + n) * R + 32 * s + 8 * g);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = min(i0 + 16 * mb + 4 * g + e, D - 1);   // rows past d are dropped below
-                sv[mb][e] = S[static_cast<int64_t>(i) * R + 16 * nb + n];
-            }
-    };
-    u32x4_t bf[KS], bf_n[KS];
-    float sv[2][4], sv_n[2][4];
-    fetch(0, bf, sv);
-#pragma unroll 1
-    for (int nb = 0; nb < NB; ++nb) {
-        if (nb + 1 < NB) fetch(nb + 1, bf_n, sv_n);
+    for (int mb = 0; mb < NB; ++mb) {
+        const int mrow = 32 * (mb >> 1) + 4 * (mb & 1) + mrow_base;
         f32x4_t acc[2] = {zero_f32x4(), zero_f32x4()};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            const u32x4_t af =
+                *reinterpret_cast<const u32x4_t *>(&ms[mrow * R + 8 * ((4 * s + g) ^ (mrow & (SW - 1)))]);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) acc[mb] = mfma_bf16(af[mb][s], bf[s], acc[mb]);
+            for (int ib = 0; ib < 2; ++ib) acc[ib] = mfma_bf16(af, bt[ib][s], acc[ib]);
+        }
+        // lane (n, g) now holds Y[i][32 (mb / 2) + 8 g + 4 (mb % 2) + e]
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int ib = 0; ib < 2; ++ib) {
+            const f32x4_t sv = raw[ib][mb >> 1][mb & 1];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ydot[mb][e] = fmaf(sv[mb][e], acc[mb][e], ydot[mb][e]);
-                ssq[mb][e] = fmaf(sv[mb][e], sv[mb][e], ssq[mb][e]);
-            }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) bf[s] = bf_n[s];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sv[mb][e] = sv_n[mb][e];
+            for (int e = 0; e < 4; ++e) ydot[ib] = fmaf(sv[e], acc[ib][e], ydot[ib]);
+        }
     }
-    // add the 16 lanes of each row (lanes g*16 .. g*16+15), fixed butterfly order
+    // add the four lanes of a row (g = 0..3), fixed butterfly order
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                ydot[mb][e] += __shfl_xor(ydot[mb][e], off, 64);
-                ssq[mb][e] += __shfl_xor(ssq[mb][e], off, 64);
-            }
-    // lane n == e writes row 16 mb + 4 g + e
+        for (int off = 16; off < 64; off <<= 1) {
+            ydot[ib] += __shfl_xor(ydot[ib], off, 64);
+            ssq[ib] += __shfl_xor(ssq[ib], off, 64);
+        }
+    // lanes g == ib write row i0 + 16 ib + n
     float term = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = i0 + 16 * mb + 4 * g + e;
-            if (n == e && i < D) {
-                const float rq = (c * c) * fmaf(static_cast<float>(K), ssq[mb][e], ydot[mb][e]);
-                rowsq[i] = rq;
-                const float vn = beta2 * v[i] + (1.f - beta2) * (rq / static_cast<float>(K));
-                const float u = 1.f / (sqrtf(vn) + eps);
-                term += rq * u * u;
-            }
+    for (int ib = 0; ib < 2; ++ib) {
+        const int i = i0 + 16 * ib + n;
+        if (g == ib && i < D) {
+            const float rq = (c * c) * fmaf(static_cast<float>(K), ssq[ib], ydot[ib]);
+            rowsq[i] = rq;
+            const float vn = beta2 * v[i] + (1.f - beta2) * (rq / static_cast<float>(K));
+            const float u = 1.f / (sqrtf(vn) + eps);
+            term += rq * u * u;
         }
+    }
     // per-workgroup partial of the controller's reduction, fixed order
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) term += __shfl_xor(term, off, 64);
@@ -178,10 +179,10 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
     SqnormPlan p;
     p.n_blocks = static_cast<int>((D + 127) / 128);
+    (void)K;
     const size_t align = 256;
     p.partial_bytes = (static_cast<size_t>(p.n_blocks) * 4 + align - 1) / align * align;
-    p.gram_bytes = static_cast<size_t>(R) * R * 2;
-    (void)K;
+    p.gram_bytes = (static_cast<size_t>(R) * R * 2 + align - 1) / align * align;
     return p;
 }
 
@@ -191,11 +192,10 @@ static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, hipStream_t st) {
     char *base = static_cast<char *>(ws);
     float *partials = reinterpret_cast<float *>(base);
     uint16_t *M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
-    hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R,
-                       static_cast<int>(a.K), M);
+    const int K = static_cast<int>(a.K);
+    hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M);
     hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
-                       static_cast<int>(a.D), static_cast<int>(a.K), M, a.c, a.v_in, a.beta2, a.eps,
-                       a.rowsq_out, partials);
+                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.rowsq_out, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_sqnorm_final(partials, p.n_blocks, a.sqnorm, st);
