@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen7b_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=0,
+                    help="streams the matrices of a step are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -110,21 +112,55 @@ def main():
         })
     ws_bytes = max(B.logra_sketch_workspace_bytes(B.MatrixDesc(s.d, s.k, r), T, code)
                    for s in wl.matrices)
-    ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
     sq_ws_bytes = max(B.logra_sqnorm_workspace_bytes(B.MatrixDesc(s.d, s.k, r), code)
                       for s in wl.matrices)
-    sq_ws = torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev)
-    # one set of microbatch buffers per (input shape, microbatch)
+    # Independent matrices run on separate streams (matrix i on stream i mod
+    # n), each stream with its own workspaces, so small projections (k, v)
+    # overlap the large ones instead of leaving most of the GPU idle.
+    n_streams = args.streams or (1 if len(mats) == 1 else 3)
+    n_streams = max(1, min(n_streams, len(mats)))
+    main = torch.cuda.current_stream()
+    lanes = []
+    for i in range(n_streams):
+        lanes.append({
+            "stream": main if i == 0 else torch.cuda.Stream(device=dev),
+            "ws": torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev),
+            "sq_ws": torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev),
+        })
+    for i, m in enumerate(mats):
+        m["lane"] = lanes[i % n_streams]
+    # Microbatch buffers: every microbatch has its own; layer stacks rotate
+    # two sets of per-layer inputs (even and odd layers), which keeps a
+    # 28- or 64-layer step within memory while consecutive layers still read
+    # different buffers. Projections that read the same activation share X.
+    def xkey(spec, mb):
+        return (spec.layer % 2, inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)
+
+    def ykey(spec, mb):
+        return (spec.layer % 2, spec.name, spec.d, mb)
+
     xbuf, ybuf = {}, {}
     for spec in wl.matrices:
         for mb in range(nmb):
-            xkey = (inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)
-            if xkey not in xbuf:
-                xbuf[xkey] = inputs.activations(wl, spec, 0, mb, device=dev)
-            ykey = (spec.matrix_id, mb)
-            ybuf[ykey] = inputs.output_grads(wl, spec, 0, mb, device=dev)
+            if xkey(spec, mb) not in xbuf:
+                xbuf[xkey(spec, mb)] = inputs.activations(wl, spec, 0, mb, device=dev)
+            if ykey(spec, mb) not in ybuf:
+                ybuf[ykey(spec, mb)] = inputs.output_grads(wl, spec, 0, mb, device=dev)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    stream = main
+
+    def fork():
+        if n_streams > 1:
+            e = torch.cuda.Event()
+            e.record(main)
+            for ln in lanes[1:]:
+                ln["stream"].wait_event(e)
+
+    def join():
+        for ln in lanes[1:]:
+            e = torch.cuda.Event()
+            e.record(ln["stream"])
+            main.wait_event(e)
 
     sketch_flop_per_step = sum(2.0 * T * r * (s.d + s.k) for s in wl.matrices) * nmb
     fold_bytes_per_step = 0.0
@@ -148,37 +184,47 @@ def main():
 
     def sketch_calls(step, m, mb, what):
         spec = m["spec"]
-        X = xbuf[(inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)]
-        dY = ybuf[(spec.matrix_id, mb)]
+        X = xbuf[xkey(spec, mb)]
+        dY = ybuf[ykey(spec, mb)]
+        ln = m["lane"]
         if what in ("project", "both"):
-            B.logra_sketch_project(m["desc"], X, ws, stream)
+            B.logra_sketch_project(m["desc"], X, ln["ws"], ln["stream"])
         if what in ("fold", "both"):
-            B.logra_sketch_fold(m["desc"], dY, m["S"], mb > 0, ws, stream)
+            B.logra_sketch_fold(m["desc"], dY, m["S"], mb > 0, ln["ws"], ln["stream"])
 
     def one_step(step, timed):
         for m in mats:
             spec = m["spec"]
             m["desc"] = B.MatrixDesc(spec.d, spec.k, r, seed=0, step=step, matrix_id=spec.matrix_id)
+        # microbatch-major, as a backward pass produces them: every matrix's
+        # sketch takes each microbatch in turn
         e0 = ev() if timed else None
-        for m in mats:
-            for mb in range(nmb):
+        fork()
+        for mb in range(nmb):
+            for m in mats:
                 sketch_calls(step, m, mb, "both")
+        join()
         e1 = ev() if timed else None
+        fork()
         for m in mats:
+            ln = m["lane"]
             B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["rowsq"],
-                                  m["sq"], sq_ws, stream)
+                                  m["sq"], ln["sq_ws"], ln["stream"])
+        join()
         e2 = ev() if timed else None
         # step controller stand-in: read every sqnorm, skip non-finite ones,
         # use the drawn scale (the controller's formula is not part of this path)
         sqs = torch.cat([m["sq"] for m in mats]).cpu().tolist()
         e3 = ev() if timed else None
+        fork()
         for m, sq in zip(mats, sqs):
             if not math.isfinite(sq):
                 skipped[0] += 1
                 continue
             scale = inputs.step_scale(wl, m["spec"], step)
             B.logra_rowadam_apply(m["desc"], code, m["S"], m["v"], m["rowsq"], m["W"], wl.lr, scale,
-                                  wl.beta2, wl.eps, stream)
+                                  wl.beta2, wl.eps, m["lane"]["stream"])
+        join()
         if timed:
             e4 = ev()
             ev_log.append(("sketch", e0, e1))
@@ -201,10 +247,12 @@ def main():
         reps = max(1, 64 // (nmb * len(mats)))
         torch.cuda.synchronize()
         a = ev()
+        fork()
         for _ in range(reps):
-            for m in mats:
-                for mb in range(nmb):
+            for mb in range(nmb):
+                for m in mats:
                     sketch_calls(0, m, mb, what)
+        join()
         b = ev()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * nmb * len(mats))
@@ -221,6 +269,7 @@ def main():
     sketch_tflops = sketch_flop_per_step / (sketch_ms * 1e-3) / 1e12
     apply_gbps = apply_bytes_per_step / (apply_ms * 1e-3) / 1e9
     fold_bytes_avg = fold_bytes_per_step / (nmb * len(mats))
+    dev_free, dev_total = torch.cuda.mem_get_info(dev)
     fold_gbps = fold_bytes_avg / (fold_ms * 1e-3) / 1e9
 
     result = {
@@ -254,6 +303,13 @@ def main():
                      "algorithmic_bytes_per_launch": round(fold_bytes_avg)},
         "state_bytes": {"sketch_plus_v": sum(4 * s.d * r + 4 * s.d for s in wl.matrices),
                         "dense_grad_fp32": sum(4 * s.d * s.k for s in wl.matrices)},
+        "memory": {"peak_allocated": torch.cuda.max_memory_allocated(dev),
+                   "device_in_use": dev_total - dev_free,
+                   "weights": sum(m["W"].numel() * m["W"].element_size() for m in mats),
+                   "microbatch_inputs": sum(t.numel() * t.element_size()
+                                            for t in list(xbuf.values()) + list(ybuf.values())),
+                   "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes))},
+        "streams": n_streams,
     }
 
     if not args.no_cpu_baseline:
