@@ -33,6 +33,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of roofline"
+# HBM bytes per fold launch measured with rocprofv3 counters (FETCH_SIZE x 2
+# + WRITE_SIZE x 1, the factors a plain device copy gives), per workload; see
+# profiles/hbm_traffic_qwen7b_up.md. Only valid for the fold kernel as it was
+# when the counters were taken.
+FOLD_TRAFFIC_BYTES = {"qwen7b_up": (92988 * 2 + 18944) * 1024}
 
 
 def parse():
@@ -299,7 +304,8 @@ def main():
                   "skipped_nonfinite": skipped[0]},
         "roofline": {"kernel": "fold_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
                      "achieved": round(fold_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(fold_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(fold_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": FOLD_TRAFFIC_BYTES.get(wl.name),
                      "algorithmic_bytes_per_launch": round(fold_bytes_avg)},
         "state_bytes": {"sketch_plus_v": sum(4 * s.d * r + 4 * s.d for s in wl.matrices),
                         "dense_grad_fp32": sum(4 * s.d * s.k for s in wl.matrices)},
