@@ -41,6 +41,10 @@ def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev):
 
 APPLY_CASES = [
     # d, k, r
+    # (1000, 4104, 256): more 256-row x 64-column units than workgroups, so a
+    # workgroup walks several units, crosses row tiles, and ends on the
+    # partial last row tile and column tile
+    (1000, 4104, 256),
     (64, 128, 32),
     (200, 520, 64),
     (136, 1000, 128),
