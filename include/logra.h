@@ -107,8 +107,11 @@ logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stre
  * logra_sketch_workspace_bytes -- device workspace that
  * logra_sketch_accumulate needs for these sizes (0 when T == 0). Returns 0
  * and sets nothing for invalid arguments (m NULL, sizes <= 0, T < 0, bad
- * dtype). The workspace holds the projected microbatch X A^T and its split
- * partial sums; it is scratch, free to reuse once the call's work has run.
+ * dtype). The workspace holds the projected microbatch X A^T, then the
+ * partial tiles that the workgroups sharing a tile of S exchange, then (when
+ * two share each tile) a few sync words that the projection zeroes and the
+ * fold leaves zero. It is scratch, free to reuse once the call's work has
+ * run; two calls that run at the same time need two workspaces.
  */
 size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dtype);
 
@@ -153,9 +156,11 @@ logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_d
  * exactly logra_sketch_accumulate: same kernels, same results.
  *   project: workspace <- X A^T (bf16 path: rounded to bf16, nearest even;
  *            fp32 path: fp32). Same arguments and errors as accumulate.
- *   fold:    S (+)= dY^T (X A^T) reading the projection from the workspace.
- *            The workspace must hold a projection of this (m, T, act_dtype)
- *            made by logra_sketch_project; fold does not check that it does.
+ *   fold:    S (+)= dY^T (X A^T) reading the projection from the workspace
+ *            (and using the rest of it as scratch). The workspace must hold a
+ *            projection of this (m, T, act_dtype) made by
+ *            logra_sketch_project; fold does not check that it does. Several
+ *            folds may follow one projection, one after another.
  * Sources: as logra_sketch_accumulate (S = G A^T factored as dY^T (X A^T)).
  */
 logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtype,
@@ -164,7 +169,7 @@ logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtyp
 logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
                                const void *dY, int64_t lddy,
                                float *S, int accumulate,
-                               const void *ws, size_t ws_bytes, void *stream);
+                               void *ws, size_t ws_bytes, void *stream);
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs

@@ -73,7 +73,7 @@ size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dt
         if (!bf16_rank_ok(m->r)) return 0;
         const Stage1Plan p = plan_stage1_bf16(T, m->k, static_cast<int>(m->r));
         const FoldPlan f = plan_fold_bf16(T, m->d, static_cast<int>(m->r));
-        return p.p_bytes + f.part_bytes;
+        return p.p_bytes + f.xbuf_bytes + f.sync_bytes;
     }
     if (act_dtype == LOGRA_F32) return workspace_sketch_f32(T, m->r);
     return 0;
@@ -122,12 +122,12 @@ static hipError_t do_project(const logra_matrix *m, int64_t T, int act_dtype, co
     const float c = inv_sqrt_rank(m->r);
     const int r = static_cast<int>(m->r);
     if (act_dtype == LOGRA_BF16)
-        return launch_project_bf16(r, T, m->k, key, c, static_cast<const uint16_t *>(X), ldx, ws, st);
+        return launch_project_bf16(r, T, m->d, m->k, key, c, static_cast<const uint16_t *>(X), ldx, ws, st);
     return launch_project_f32(r, T, m->k, key, c, static_cast<const float *>(X), ldx, ws, st);
 }
 
 static hipError_t do_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
-                          int64_t lddy, float *S, int accumulate, const void *ws, hipStream_t st) {
+                          int64_t lddy, float *S, int accumulate, void *ws, hipStream_t st) {
     if (T == 0) return accumulate ? hipSuccess : launch_fill_zero(S, m->d * m->r, st);
     const int r = static_cast<int>(m->r);
     if (act_dtype == LOGRA_BF16)
@@ -146,7 +146,7 @@ logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtyp
 }
 
 logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
-                               int64_t lddy, float *S, int accumulate, const void *ws,
+                               int64_t lddy, float *S, int accumulate, void *ws,
                                size_t ws_bytes, void *stream) {
     logra_status e = check_sketch(m, T, act_dtype);
     if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);

@@ -5,43 +5,74 @@
 // eight-GPU node", section "Why it matters").
 //
 // This is the dominant, HBM-bound kernel of the sketch: dY (T x d) is the big
-// stream and every byte of it meets all r = 256 columns of P. Design:
-//   * One workgroup per compute unit, each owning a contiguous range of 4-5
-//     blocks of 16 rows of S (64-80 rows) and all r columns, so dY is read from
-//     HBM exactly once and the row ranges are balanced over the 256 CUs. When d
-//     is too small to give every CU work, the token range is split as well and
-//     a second pass adds the partial tiles in a fixed order.
+// stream and every byte of it meets all r = 256 columns of P. What limits it
+// on gfx950 is the bytes each compute unit pulls through its vector memory
+// path: its own dY rows, plus all of P for the tokens it covers. Design:
+//   * A tile is up to 10 blocks of 16 rows of S and all r columns; n_split
+//     workgroups ("members") share a tile, each over one contiguous range of
+//     the token steps. Splitting the tokens of taller tiles cuts the P bytes
+//     per compute unit (for d = 18944: 128 tiles of 144-160 rows x 2 token
+//     halves rather than 256 tiles of 64-80 rows x all tokens), and dY is
+//     still read once. Kernel instances are built for tiles of at most 5 or
+//     at most 10 blocks; the waves compute every block of the instance but the
+//     last unconditionally (products past the tile are never stored), which
+//     keeps the unrolled steps free of branches.
 //   * dY is token-major, but the MFMA wants 8 consecutive tokens per lane. Each
 //     thread streams 16-byte chunks of dY rows (8 columns of one token) into a
-//     3-slot LDS ring, 4 steps of 32 tokens ahead in registers; the waves then
-//     read operand fragments with the gfx950 transpose read ds_read_b64_tr_b16
-//     (one 4 x 16 block per 16-lane group, column j to lane j). LDS rows are 80
-//     elements (160 bytes) apart, which keeps the four rows of each block on
-//     disjoint banks.
-//   * P is stored by stage 1 in operand-fragment order, so its fragments come
-//     straight from L2 into registers, two steps ahead. The four waves split
-//     the r columns (64 each), so no P fragment is read twice in a workgroup.
+//     3-slot LDS ring, several steps of 32 tokens ahead in registers; the waves
+//     then read operand fragments with the gfx950 transpose read
+//     ds_read_b64_tr_b16 (one 4 x 16 block per 16-lane group, column j to lane
+//     j). P is stored by stage 1 in operand-fragment order, so its fragments
+//     come straight from L2 into registers. The four waves split the r columns
+//     (64 each), so no P fragment is read twice in a workgroup.
 //   * Barriers wait only for LDS traffic (workgroup fences on the local address
 //     space), so the global prefetches stay in flight across them.
+//   * Two members per tile add their partials without a second kernel: the
+//     first finalizes the first half of the tile's row blocks, the second the
+//     rest. Each writes its accumulators of the other's blocks to an exchange
+//     buffer as raw MFMA fragments (1 KB per wave and block, device-coherent
+//     stores), raises its flag, waits for the other's flag, and forms
+//     S = [S +] (part_0 + part_1) for its rows; fp32 addition commutes, so the
+//     result does not depend on which member finishes first. Members take
+//     tickets from a counter when they start and a tile's two members hold
+//     consecutive tickets, so a member only ever waits for a workgroup that has
+//     already started: no co-residency beyond two workgroups is assumed.
+//     Waits are bounded; on time-out the rows are written as NaN rather than
+//     hanging. Stage 1 zeroes the counter and flags before each fold and the
+//     fold leaves them zero.
+//   * More members per tile (small d, so that the grid still fills the chip)
+//     each write their whole partial tile, and fold_reduce_kernel adds them in
+//     member order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace logra {
 
-constexpr int kFoldMaxBlocks = 5;     // 16-row blocks per workgroup tile (up to 80 rows)
-constexpr int kFoldLdsRow = 80;       // bf16 elements per LDS row of a ring slot
 constexpr int kFoldSlots = 3;         // LDS ring slots (one step of 32 tokens each)
-constexpr int kFoldPrefetch = 8;      // steps of dY held in registers ahead of use
+constexpr int kFoldMaxSplit = 32;     // members per tile (most)
 constexpr int kXcds = 8;              // gfx950: workgroup ids go round-robin over 8 XCDs
-constexpr int kFoldTargetWGs = 256;   // one workgroup per compute unit
+constexpr int kFoldWGs = 256;         // one workgroup per compute unit
+constexpr int kFoldSpinLimit = 1 << 20;   // polls of a member's flag before giving up
 
-template <int R>
+// Shape of one kernel instance. MAXB (5 or 10) bounds the 16-row blocks of a
+// tile; tiles are planned to hold MAXB or MAXB - 1 blocks where d allows,
+// and the waves compute every block but the last unconditionally (products
+// of blocks past the tile are never stored), which keeps the unrolled steps
+// free of branches.
+template <int R, int MAXB>
 struct FoldShape {
     static constexpr int NB = R / 16;            // 16-wide column blocks of r
     static constexpr int WN = NB < 4 ? NB : 4;   // waves across r
     static constexpr int NBW = NB / WN;          // column blocks per wave
     static constexpr int WM = 4 / WN;            // waves across row blocks
-    static constexpr int MBW = (kFoldMaxBlocks + WM - 1) / WM;   // row blocks per wave (max)
+    static constexpr int MBW = (MAXB + WM - 1) / WM;   // row blocks per wave
+    static constexpr int LDS_ROW = 16 * MAXB;    // bf16 elements per LDS token row of a ring slot
+    static constexpr int NCH = (32 * 2 * MAXB + 255) / 256;   // dY chunks per thread per step
+    static constexpr int PF = MAXB > 5 ? 4 : 8;  // steps of dY and P held in registers ahead of use
+    static constexpr int HALF = (MBW + 1) / 2;   // a wave's row blocks finalized by the first of two members
+    static constexpr int STAGE = R >= 256 ? 80 : 160;   // rows of the epilogue staging tile
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -62,22 +93,34 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int R>
+// Cache policy of the exchange traffic: device scope (the SC1 bit, what
+// agent-scope atomic loads and stores compile to on gfx950), so a partial
+// written on one XCD is read correctly from another.
+constexpr int kDeviceScope = 16;
+
+// How the members of a tile add their partials: one member (nothing to
+// add); two, exchanging MFMA fragments within the kernel; or more, each
+// writing its partial tile for fold_reduce_kernel to add.
+enum FoldMode { kFoldSingle = 0, kFoldPair = 1, kFoldPartial = 2 };
+
+template <int R, int MAXB, int MODE>
 __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
-    int p_blocks, float *__restrict__ S, float *__restrict__ part, int accumulate, int nblk,
-    int n_wg_d, int steps_per) {
-    using Sh = FoldShape<R>;
-    constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = kFoldPrefetch;
-    constexpr int kSlot = 32 * kFoldLdsRow;             // one step: 32 token rows
-    constexpr int kTileRows = kFoldMaxBlocks * 16;      // rows of S per workgroup (max)
-    constexpr int kTileLd = R + 4;                      // fp32 row stride of the output tile in LDS
+    int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
+    int accumulate, int nblk, int n_tiles, int n_split, int steps_per) {
+    using Sh = FoldShape<R, MAXB>;
+    constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = Sh::PF, NCH = Sh::NCH;
+    constexpr int kLdsRow = Sh::LDS_ROW;
+    constexpr int kSlot = 32 * kLdsRow;                 // one step: 32 token rows
+    constexpr int kTileLd = R + 4;                      // fp32 row stride of the staging tile in LDS
     constexpr int kRowChunks = R / 4;                   // 16-byte chunks per row of S
-    constexpr int kOutChunks = (kTileRows * kRowChunks + 255) / 256;   // per thread
+    constexpr int kStage = Sh::STAGE;
+    constexpr int kOutChunks = (kStage * kRowChunks + 255) / 256;   // per thread per staged pass
     constexpr int kRingBytes = kFoldSlots * kSlot * 2;
-    constexpr int kTileBytes = kTileRows * kTileLd * 4;
-    // The dY ring during the loop, the output tile in the epilogue.
+    constexpr int kTileBytes = kStage * kTileLd * 4;
+    // The dY ring during the loop, the staging tile in the epilogue.
     __shared__ __attribute__((aligned(16))) char smem[kRingBytes > kTileBytes ? kRingBytes : kTileBytes];
+    __shared__ int s_word;
     uint16_t *lds = reinterpret_cast<uint16_t *>(smem);
     float *tile = reinterpret_cast<float *>(smem);
 
@@ -86,23 +129,57 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Sh::WN, wn = wave % Sh::WN;
     const int i16 = lane & 15, g = lane >> 4;
-    const int sp = blockIdx.y;
-    // Consecutive row tiles go to the same XCD (ids are dealt round-robin over
-    // the XCDs), so the cache lines two neighbouring tiles share are fetched
-    // into one L2 only.
-    const int wg = (n_wg_d % kXcds == 0)
-                       ? (blockIdx.x % kXcds) * (n_wg_d / kXcds) + blockIdx.x / kXcds
-                       : static_cast<int>(blockIdx.x);
-    const int b0 = static_cast<int>((static_cast<int64_t>(wg) * nblk) / n_wg_d);
-    const int b1 = static_cast<int>((static_cast<int64_t>(wg + 1) * nblk) / n_wg_d);
+    const int G = n_tiles * n_split;
+
+    // Tile and member: a ticket when members exchange partials; otherwise
+    // the workgroup id, with consecutive tiles on one XCD (ids are dealt
+    // round-robin over the XCDs) so the cache lines that neighbouring tiles
+    // share are fetched into one L2.
+    int ticket;
+    if (MODE == kFoldPair) {
+        if (tid == 0) {
+            const unsigned t = static_cast<unsigned>(
+                __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            // in range even if the counter was not zeroed (no projection made
+            // in this workspace): then the results are undefined, not a fault
+            const int tk = static_cast<int>(t % static_cast<unsigned>(G));
+            if (tk == G - 1) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_word = tk;
+        }
+        __syncthreads();
+        ticket = __builtin_amdgcn_readfirstlane(s_word);
+    } else {
+        ticket = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
+                                  : static_cast<int>(blockIdx.x);
+    }
+    const int ti = ticket / n_split, mem = ticket % n_split;
+    const int b0 = static_cast<int>((static_cast<int64_t>(ti) * nblk) / n_tiles);
+    const int b1 = static_cast<int>((static_cast<int64_t>(ti + 1) * nblk) / n_tiles);
     const int nmb = b1 - b0;
     const int d0 = b0 * 16;
+    const int rows = nmb * 16;
     const int cpr = nmb * 2;              // 16-byte chunks per token row of the tile
     const int nchunk = 32 * cpr;          // chunks per step of 32 tokens
     const int nsteps = (T + 31) >> 5;
-    const int s_begin = sp * steps_per;
+    const int s_begin = min(nsteps, mem * steps_per);
     const int s_end = min(nsteps, s_begin + steps_per);
     const int l_base = wn * NBW * 16;
+
+    // Rows this member finalizes: with two members, the first finalizes the
+    // first HALF row blocks of every wave (rows [0, 16 WM HALF)) and the
+    // second the rest, and their partials move as MFMA fragments (1 KB per
+    // wave and block, no staging); with more members, consecutive row ranges,
+    // and the partials move as rows.
+    constexpr int kHalf = Sh::HALF;
+    int own0, own1;
+    if (MODE == kFoldPair) {
+        own0 = mem == 0 ? 0 : min(16 * WM * kHalf, rows);
+        own1 = mem == 0 ? min(16 * WM * kHalf, rows) : rows;
+    } else {
+        own0 = 0;
+        own1 = MODE == kFoldSingle ? rows : 0;
+    }
+
 
     // Buffer views: loads past num_records return zero and stores there are
     // dropped, which masks the token tail, the phantom steps after s_end,
@@ -113,26 +190,26 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(P), 0, static_cast<int>(static_cast<int64_t>(p_blocks) * R * 64),
         0x00020000);
-    float *dst = part ? part + static_cast<size_t>(sp) * D * R : S;
     const __amdgpu_buffer_rsrc_t s_rs =
-        __builtin_amdgcn_make_buffer_rsrc(dst, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(S, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
 
-    // The (at most two) 16-byte dY chunks this thread moves per step. Chunk
+    // The (up to NCH) 16-byte dY chunks this thread moves per step. Chunk
     // counts are multiples of 64, so whether a wave has a chunk is uniform
     // across the wave.
-    const bool has[2] = {wave * 64 < nchunk, wave * 64 + 256 < nchunk};
-    uint32_t q_goff[2];   // byte offset of the chunk in token row 0
-    int q_loff[2];        // element offset in a slot
-    bool q_ok[2];
+    bool has[NCH];
+    uint32_t q_goff[NCH];   // byte offset of the chunk in token row 0
+    int q_loff[NCH];        // element offset in a slot
+    bool q_ok[NCH];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NCH; ++k) {
         const int q = tid + 256 * k;
+        has[k] = wave * 64 + 256 * k < nchunk;
         const bool on = q < nchunk;
         const int t = on ? q / cpr : 0;
         const int c = on ? q - t * cpr : 0;
         q_ok[k] = on && d0 + 8 * c < D;
         q_goff[k] = static_cast<uint32_t>((static_cast<int64_t>(t) * lddy + d0 + 8 * c) * 2);
-        q_loff[k] = t * kFoldLdsRow + 8 * c;
+        q_loff[k] = t * kLdsRow + 8 * c;
     }
     const uint32_t row_step_bytes = static_cast<uint32_t>(lddy * 2 * 32);   // one step of 32 tokens
     auto gload = [&](int s, int k) -> u32x4_t {
@@ -151,24 +228,20 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             b[nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(p_rs, off, 0, 0));
         }
     };
+    // every block but the last is read whatever the tile height (stale LDS
+    // past the tile feeds products that are never stored)
     auto aread = [&](int s, u32x4_t (&a)[MBW]) {
         const uint16_t *base = &lds[(s % kFoldSlots) * kSlot];
 #pragma unroll
         for (int j = 0; j < MBW; ++j) {
-            // blocks past this tile read stale LDS; their products are never stored
             const int mb = wm + j * WM;
-            const uint16_t *p = base + (8 * g + (i16 >> 2)) * kFoldLdsRow + 16 * mb + 4 * (i16 & 3);
-            const u32x2_t lo = lds_read_tr(p);
-            const u32x2_t hi = lds_read_tr(p + 4 * kFoldLdsRow);
-            a[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+            if (j < MBW - 1 || mb < nmb) {
+                const uint16_t *p = base + (8 * g + (i16 >> 2)) * kLdsRow + 16 * mb + 4 * (i16 & 3);
+                const u32x2_t lo = lds_read_tr(p);
+                const u32x2_t hi = lds_read_tr(p + 4 * kLdsRow);
+                a[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+            }
         }
-    };
-    // Output chunk c of this thread: row (tid + 256 c) / kRowChunks of the
-    // tile, 4 columns from 4 * ((tid + 256 c) % kRowChunks).
-    auto out_off = [&](int c) -> uint32_t {
-        const int q = tid + 256 * c;
-        const int row = q / kRowChunks, col = 4 * (q % kRowChunks);
-        return row < nmb * 16 ? static_cast<uint32_t>(((d0 + row) * R + col) * 4) : kOob;
     };
 
     f32x4_t acc[MBW][NBW];
@@ -180,26 +253,20 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     // Prefetch ring: dY chunks and P fragments of the next PF steps, issued
     // in step order, so that every wait below is for a load issued PF - 1 or
     // PF steps earlier (loads complete in issue order).
-    u32x4_t raw[PF][2];
+    u32x4_t raw[PF][NCH];
     u32x4_t pb[PF][NBW];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) raw[p][k] = gload(s_begin + p, k);
+        for (int k = 0; k < NCH; ++k) raw[p][k] = gload(s_begin + p, k);
         bload(s_begin + p, pb[p]);
     }
-    // The old S tile, read while the stream runs (the first waits are for
-    // the loads above, issued before these).
-    const bool add_old = accumulate && !part;
-    u32x4_t old[kOutChunks];
-#pragma unroll
-    for (int c = 0; c < kOutChunks; ++c)
-        old[c] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(s_rs, add_old ? out_off(c) : kOob, 0, 0));
 
     u32x4_t a_cur[MBW], a_nxt[MBW];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int j = 0; j < MBW; ++j) a_cur[j] = a_nxt[j] = zero_u32x4();
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
         lstore(s_begin, raw[0][k], k);
         raw[0][k] = gload(s_begin + PF, k);
     }
@@ -215,7 +282,7 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             // raw[(p + 1) % PF] holds the dY of step s + 1 and pb[p] the P
             // fragments of step s (s0 - s_begin is a multiple of PF)
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < NCH; ++k) {
                 lstore(s + 1, raw[(p + 1) % PF][k], k);
                 raw[(p + 1) % PF][k] = gload(s + 1 + PF, k);
             }
@@ -223,7 +290,7 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             aread(s + 1, a_nxt);
 #pragma unroll
             for (int j = 0; j < MBW; ++j) {
-                if (wm + j * WM < nmb) {
+                if (j < MBW - 1 || wm + j * WM < nmb) {
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
                         acc[j][nb] = mfma_bf16(a_cur[j], pb[p][nb], acc[j][nb]);
@@ -235,34 +302,200 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         }
     }
 
-    // Epilogue: the accumulators go through LDS into row-major order, so that
-    // the read-modify-write of S is whole 16-byte chunks of rows. Lane
-    // (i16, g) of row block mb holds rows 16 mb + 4 g + e, column
-    // l_base + 16 nb + i16.
-    lds_barrier();   // every wave is done with the ring
+    // ---- epilogue. The accumulators go through LDS into row-major order in
+    // passes of up to kStage rows, so that S moves in whole 16-byte row
+    // chunks. Lane (i16, g) of row block mb holds rows 16 mb + 4 g + e,
+    // column l_base + 16 nb + i16.
+
+    // stage rows [r0, r1) of the tile
+    auto stage = [&](int r0, int r1) {
+        lds_barrier();   // the previous user of the LDS is done
 #pragma unroll
-    for (int j = 0; j < MBW; ++j) {
-        const int mb = wm + j * WM;
-        if (mb < nmb) {
+        for (int j = 0; j < MBW; ++j) {
+            const int mb = wm + j * WM;
+            if (mb < nmb && 16 * mb + 16 > r0 && 16 * mb < r1) {
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * mb + 4 * g + e;
+                    if (row >= r0 && row < r1) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    tile[(16 * mb + 4 * g + e) * kTileLd + l_base + 16 * nb + i16] = acc[j][nb][e];
+                        for (int nb = 0; nb < NBW; ++nb)
+                            tile[(row - r0) * kTileLd + l_base + 16 * nb + i16] = acc[j][nb][e];
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    };
+    // Chunk c of this thread in a pass from row r0: tile row
+    // r0 + (tid + 256 c) / kRowChunks, columns 4 ((tid + 256 c) % kRowChunks) .. +3.
+    auto chunk_row = [&](int r0, int c) { return r0 + (tid + 256 * c) / kRowChunks; };
+    auto chunk_col = [&](int c) { return 4 * ((tid + 256 * c) % kRowChunks); };
+    auto staged = [&](int r0, int c) -> f32x4_t {
+        const int lr = min(chunk_row(r0, c) - r0, kStage - 1);
+        return *reinterpret_cast<const f32x4_t *>(&tile[lr * kTileLd + chunk_col(c)]);
+    };
+    // byte offset of (tile row, column) in a d x r fp32 matrix
+    auto s_off = [&](int row, int col) -> uint32_t {
+        return static_cast<uint32_t>(((d0 + row) * R + col) * 4);
+    };
+    // byte offset of chunk c of a pass over rows [r0, r1) in a d x r matrix (kOob outside)
+    auto c_off = [&](int r0, int r1, int c) -> uint32_t {
+        const int row = chunk_row(r0, c);
+        return (row < r1 && d0 + row < D) ? s_off(row, chunk_col(c)) : kOob;
+    };
+
+    int *flags = sync + 1;
+    int *done = flags + n_tiles * n_split;
+    const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(xbuf, 0, x_bytes, 0x00020000);
+    const uint32_t x_stride = static_cast<uint32_t>(static_cast<int64_t>(D) * R * 4);   // rows layout
+    // fragment (member q, row block mb, column block nb of this wave) in the
+    // fragment layout: 1 KB per wave, 16 bytes per lane
+    auto x_frag = [&](int q, int mb, int nb) -> uint32_t {
+        return static_cast<uint32_t>(((((ti * 2 + q) * MAXB + mb) * Sh::WN + wn) * NBW + nb) * 1024 + lane * 16);
+    };
+
+    if (MODE == kFoldPair) {
+        // 1. this member's fragments of the blocks the other finalizes,
+        // straight from the accumulators
+#pragma unroll
+        for (int j = 0; j < MBW; ++j) {
+            const int mb = wm + j * WM;
+            if (mb < nmb && (j < kHalf) == (mem == 1)) {
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[j][nb]), x_rs,
+                                                          x_frag(mem, mb, nb), 0, kDeviceScope);
+            }
+        }
+    } else if (MODE == kFoldPartial) {
+        // this member's partial of the whole tile, for fold_reduce_kernel
+        for (int r0 = 0; r0 < rows; r0 += kStage) {
+            const int r1 = min(r0 + kStage, rows);
+            stage(r0, r1);
+#pragma unroll
+            for (int c = 0; c < kOutChunks; ++c) {
+                const uint32_t off = c_off(r0, r1, c);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, staged(r0, c)), x_rs,
+                                                      off == kOob ? kOob : off + mem * x_stride, 0, 0);
+            }
+        }
+        return;
+    }
+    if (MODE == kFoldPair) {
+        // 2. raise the flag once every thread's stores are complete
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(flags + ti * n_split + mem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // 3. finalize the own rows, in passes of up to kStage rows (a single pass
+    // whenever n_split > 1): add the other members' partials, stage, then
+    // read-modify-write S.
+    for (int r0 = own0; r0 < own1; r0 += kStage) {
+        const int r1 = min(r0 + kStage, own1);
+        bool timed_out = false;
+        if (MODE == kFoldPair) {
+            // wait for the other members' partials
+            if (tid == 0) {
+                int ok = 1;
+                for (int q = 0; q < n_split && ok; ++q) {
+                    if (q == mem) continue;
+                    int spins = 0;
+                    while (__hip_atomic_load(flags + ti * n_split + q, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                        if (++spins > kFoldSpinLimit) {
+                            ok = 0;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                s_word = ok;
+            }
+            __syncthreads();
+            timed_out = s_word == 0;
+        }
+        // S = [S +] v for the chunks of the pass, the old S loads all in flight
+        // first (unless the staged values already hold it)
+        auto finish_all = [&](auto &&value, bool add_old) {
+            u32x4_t old[kOutChunks];
+#pragma unroll
+            for (int c = 0; c < kOutChunks; ++c)
+                old[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
+#pragma unroll
+            for (int c = 0; c < kOutChunks; ++c) {
+                f32x4_t v = value(c);
+                if (add_old) v = __builtin_bit_cast(f32x4_t, old[c]) + v;
+                if (timed_out)
+                    v = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), s_rs, c_off(r0, r1, c), 0, 0);
+            }
+        };
+        if (MODE == kFoldPair) {
+            // the other member's fragments of the own blocks, all in flight
+            // before they are added during staging; part_0 + part_1 is the
+            // same sum whichever member adds it
+            auto pair = [&](auto j0c, auto j1c) {
+                constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
+                f32x4_t x[kHalf][NBW];
+#pragma unroll
+                for (int j = J0; j < J1; ++j) {
+                    const int mb = wm + j * WM;
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+                        x[j - J0][nb] = __builtin_bit_cast(
+                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                         x_rs, mb < nmb ? x_frag(1 - mem, mb, nb) : kOob, 0, kDeviceScope));
+                }
+                // stage the own rows (all of blocks J0 .. J1 - 1) as acc + x
+                lds_barrier();   // the previous user of the LDS is done
+#pragma unroll
+                for (int j = J0; j < J1; ++j) {
+                    const int mb = wm + j * WM;
+                    if (mb < nmb) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int row = 16 * mb + 4 * g + e;
+#pragma unroll
+                            for (int nb = 0; nb < NBW; ++nb)
+                                tile[(row - r0) * kTileLd + l_base + 16 * nb + i16] =
+                                    acc[j][nb][e] + x[j - J0][nb][e];
+                        }
+                    }
+                }
+                lds_barrier();
+            };
+            if (mem == 0)
+                pair(std::integral_constant<int, 0>{}, std::integral_constant<int, kHalf>{});
+            else
+                pair(std::integral_constant<int, kHalf>{}, std::integral_constant<int, MBW>{});
+            finish_all([&](int c) { return staged(r0, c); }, accumulate != 0);
+        } else {
+            stage(r0, r1);
+            finish_all([&](int c) { return staged(r0, c); }, accumulate != 0);
         }
     }
-    lds_barrier();
-#pragma unroll
-    for (int c = 0; c < kOutChunks; ++c) {
-        const int q = tid + 256 * c;
-        const int row = min(q / kRowChunks, kTileRows - 1), col = 4 * (q % kRowChunks);
-        f32x4_t v = *reinterpret_cast<const f32x4_t *>(&tile[row * kTileLd + col]);
-        if (add_old) v += __builtin_bit_cast(f32x4_t, old[c]);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), s_rs, out_off(c), 0, 0);
+
+    if (MODE == kFoldPair) {
+        // 4. the last member of the tile to finish clears the tile's flags
+        // for the next fold (no member polls them any more)
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(done + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == n_split - 1) {
+                for (int q = 0; q < n_split; ++q)
+                    __hip_atomic_store(flags + ti * n_split + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(done + ti, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
-// S = [S +] (part_0 + part_1 + ...), token splits added in order.
+// S = [S +] (part_0 + part_1 + ...): the members' partial tiles added in
+// member order (small d, more than two members per tile).
 __global__ __launch_bounds__(256) void fold_reduce_kernel(const float *__restrict__ part, int n_split,
                                                           int64_t n, float *__restrict__ S,
                                                           int accumulate) {
@@ -280,52 +513,78 @@ FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R) {
     if (T <= 0) return p;
     p.nblk = static_cast<int>((D + 15) / 16);
     const int nsteps = static_cast<int>((T + 31) / 32);
-    if (p.nblk >= kFoldTargetWGs * 4) {
-        p.n_wg_d = p.nblk > kFoldTargetWGs * kFoldMaxBlocks
-                       ? (p.nblk + kFoldMaxBlocks - 1) / kFoldMaxBlocks
-                       : kFoldTargetWGs;
-        p.n_split = 1;
+    if (p.nblk >= 2 * kFoldWGs) {
+        // tiles over two token halves when there are enough steps to split,
+        // otherwise tiles over all tokens; at most 10 blocks a tile
+        const int by_height = (p.nblk + 9) / 10;
+        if (nsteps >= 8) {
+            p.n_split = 2;
+            p.n_tiles = by_height > kFoldWGs / 2 ? by_height : kFoldWGs / 2;
+        } else {
+            p.n_split = 1;
+            p.n_tiles = by_height > kFoldWGs ? by_height : kFoldWGs;
+        }
     } else {
-        p.n_wg_d = (p.nblk + 3) / 4;
-        int ns = kFoldTargetWGs / p.n_wg_d;
-        // keep the partial tiles no larger than the dY they replace, and at
-        // least 4 steps per split
+        // small d: tiles of 4 blocks, the tokens split so that the grid fills
+        // the compute units, keeping the exchanged partials no larger than the
+        // dY they replace and at least 4 steps per member
+        p.n_tiles = (p.nblk + 3) / 4;
+        int ns = kFoldWGs / p.n_tiles;
         const int64_t cap_bytes = T / (2 * R);
         if (ns > cap_bytes) ns = static_cast<int>(cap_bytes);
         if (ns > nsteps / 4) ns = nsteps / 4;
+        if (ns > kFoldMaxSplit) ns = kFoldMaxSplit;
         if (ns < 1) ns = 1;
         p.n_split = ns;
     }
+    p.max_blocks = (p.nblk + p.n_tiles - 1) / p.n_tiles <= 5 ? 5 : 10;
     p.steps_per = (nsteps + p.n_split - 1) / p.n_split;
     p.n_split = (nsteps + p.steps_per - 1) / p.steps_per;
-    p.part_bytes = p.n_split > 1 ? static_cast<size_t>(p.n_split) * D * R * 4 : 0;
+    const size_t align = 256;
+    if (p.n_split == 2) {
+        // fragments of every block of every tile, then the sync words
+        p.xbuf_bytes = (static_cast<size_t>(p.n_tiles) * 2 * p.max_blocks * 16 * R * 4 + align - 1) / align * align;
+        p.sync_words = 1 + p.n_tiles * p.n_split + p.n_tiles;
+        p.sync_bytes = (static_cast<size_t>(p.sync_words) * 4 + align - 1) / align * align;
+    } else if (p.n_split > 2) {
+        // one d x r partial per member
+        p.xbuf_bytes = (static_cast<size_t>(p.n_split) * D * R * 4 + align - 1) / align * align;
+    }
     return p;
 }
 
 template <int R>
 static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy, const uint16_t *P,
-                         int p_blocks, float *S, int accumulate, float *part, hipStream_t st) {
+                         int p_blocks, float *S, int accumulate, void *scratch, hipStream_t st) {
     const FoldPlan p = plan_fold_bf16(T, D, R);
-    float *dst_part = p.n_split > 1 ? part : nullptr;
-    hipLaunchKernelGGL(fold_bf16_kernel<R>, dim3(p.n_wg_d, p.n_split), dim3(256), 0, st, dY, lddy,
-                       static_cast<int>(T), static_cast<int>(D), P, p_blocks, S, dst_part, accumulate, p.nblk,
-                       p.n_wg_d, p.steps_per);
-    if (p.n_split > 1) {
+    float *xbuf = static_cast<float *>(scratch);
+    int *sync = reinterpret_cast<int *>(static_cast<char *>(scratch) + p.xbuf_bytes);
+    auto kernel = fold_bf16_kernel<R, 5, kFoldSingle>;
+    if (p.n_split > 2)
+        kernel = fold_bf16_kernel<R, 5, kFoldPartial>;   // small d: tiles of at most 4 blocks
+    else if (p.n_split == 2)
+        kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldPair> : fold_bf16_kernel<R, 10, kFoldPair>;
+    else if (p.max_blocks == 10)
+        kernel = fold_bf16_kernel<R, 10, kFoldSingle>;
+    hipLaunchKernelGGL(kernel, dim3(p.n_tiles * p.n_split), dim3(256), 0, st, dY, lddy, static_cast<int>(T),
+                       static_cast<int>(D), P, p_blocks, S, xbuf, static_cast<int>(p.xbuf_bytes), sync, accumulate,
+                       p.nblk, p.n_tiles, p.n_split, p.steps_per);
+    if (p.n_split > 2) {
         const int64_t n = D * R;
-        hipLaunchKernelGGL(fold_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, part,
-                           p.n_split, n, S, accumulate);
+        hipLaunchKernelGGL(fold_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, xbuf, p.n_split, n, S,
+                           accumulate);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
-                                  float *part, hipStream_t st) {
+                                  void *scratch, hipStream_t st) {
     switch (R) {
-    case 32: return fold_r<32>(T, D, dY, lddy, P, p_blocks, S, accumulate, part, st);
-    case 64: return fold_r<64>(T, D, dY, lddy, P, p_blocks, S, accumulate, part, st);
-    case 128: return fold_r<128>(T, D, dY, lddy, P, p_blocks, S, accumulate, part, st);
-    case 256: return fold_r<256>(T, D, dY, lddy, P, p_blocks, S, accumulate, part, st);
+    case 32: return fold_r<32>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
+    case 64: return fold_r<64>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
+    case 128: return fold_r<128>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
+    case 256: return fold_r<256>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -18,20 +18,25 @@ struct Stage1Plan {
 
 Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R);
 
-// Work split of the fold S (+)= dY^T P (bf16 path): n_wg_d workgroups over the
-// nblk 16-row blocks of S, times n_split ranges of steps_per 32-token steps.
-// With n_split > 1 the partial tiles (n_split x d x r fp32) go to the workspace.
+// Work split of the fold S (+)= dY^T P (bf16 path): n_tiles row tiles over
+// the nblk 16-row blocks of S, times n_split members per tile, each over
+// steps_per 32-token steps. With n_split > 1 the members exchange partial
+// tiles (xbuf: n_split x d x r fp32) and synchronise through sync_words ints
+// (sync); both follow P in the sketch workspace.
 struct FoldPlan {
     int nblk = 0;
-    int n_wg_d = 0;
+    int n_tiles = 0;
     int n_split = 0;
     int steps_per = 0;
-    size_t part_bytes = 0;
+    int max_blocks = 0;       // 16-row blocks per tile the kernel instance is built for (5 or 10)
+    int sync_words = 0;
+    size_t xbuf_bytes = 0;
+    size_t sync_bytes = 0;
 };
 FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
-                                  float *part, hipStream_t st);
+                                  void *scratch, hipStream_t st);
 size_t workspace_sketch_f32(int64_t T, int64_t R);
 int apply_blocks_f32(int64_t D);
 
@@ -48,10 +53,10 @@ hipError_t launch_sign_words(uint64_t key, int R, int K, uint64_t *words, hipStr
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t st);
 
 // stage 1: P = c X Sigma^T into the workspace; stage 2: S (+)= dY^T P from it.
-hipError_t launch_project_bf16(int R, int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
-                               int64_t ldx, void *ws, hipStream_t st);
+hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t key, float c,
+                               const uint16_t *X, int64_t ldx, void *ws, hipStream_t st);
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                            float *S, int accumulate, const void *ws, hipStream_t st);
+                            float *S, int accumulate, void *ws, hipStream_t st);
 hipError_t launch_project_f32(int R, int64_t T, int64_t K, uint64_t key, float c, const float *X,
                               int64_t ldx, void *ws, hipStream_t st);
 hipError_t launch_fold_f32(int R, int64_t T, int64_t D, const float *dY, int64_t lddy, float *S,

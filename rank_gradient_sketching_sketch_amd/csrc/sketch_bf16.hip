@@ -47,7 +47,8 @@ struct Stage1Shape {
 template <int R>
 __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx,
                                                           int T, int K, uint64_t key, float c,
-                                                          uint16_t *__restrict__ P) {
+                                                          uint16_t *__restrict__ P, int *__restrict__ sync,
+                                                          int n_sync) {
     using Sh = Stage1Shape<R>;
     constexpr int RT = Sh::RT, NB = Sh::NB, PF = kS1Prefetch;
     constexpr int kTableBytes = kS1Waves * kS1Words * RT * 8;
@@ -59,6 +60,9 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The fold that follows in this workspace starts from zeroed sync words.
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = tid; i < n_sync; i += 64 * kS1Waves) sync[i] = 0;
     const int i16 = lane & 15, g = lane >> 4;
     const int tb = blockIdx.x;                 // 32-token block
     const int l0 = blockIdx.y * RT;            // first sign column of the tile
@@ -189,38 +193,40 @@ Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R) {
 }
 
 template <int R>
-static hipError_t project_bf16_r(int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
+static hipError_t project_bf16_r(int64_t T, int64_t D, int64_t K, uint64_t key, float c, const uint16_t *X,
                                  int64_t ldx, void *ws, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
+    const FoldPlan f = plan_fold_bf16(T, D, R);
     uint16_t *P = static_cast<uint16_t *>(ws);
+    int *sync = reinterpret_cast<int *>(static_cast<char *>(ws) + p.p_bytes + f.xbuf_bytes);
     hipLaunchKernelGGL(stage1_bf16_kernel<R>, dim3(p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
-                       static_cast<int>(T), static_cast<int>(K), key, c, P);
+                       static_cast<int>(T), static_cast<int>(K), key, c, P, sync, f.sync_words);
     return hipGetLastError();
 }
 
 template <int R>
 static hipError_t fold_bf16_r(int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                              float *S, int accumulate, const void *ws, hipStream_t st) {
+                              float *S, int accumulate, void *ws, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
-    const char *base = static_cast<const char *>(ws);
+    char *base = static_cast<char *>(ws);
     const uint16_t *P = reinterpret_cast<const uint16_t *>(base);
-    float *part = reinterpret_cast<float *>(const_cast<char *>(base) + p.p_bytes);
-    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, p.t_blocks, S, accumulate, part, st);
+    void *scratch = base + p.p_bytes;   // exchange buffer, then the sync words
+    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, p.t_blocks, S, accumulate, scratch, st);
 }
 
-hipError_t launch_project_bf16(int R, int64_t T, int64_t K, uint64_t key, float c, const uint16_t *X,
-                               int64_t ldx, void *ws, hipStream_t st) {
+hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t key, float c,
+                               const uint16_t *X, int64_t ldx, void *ws, hipStream_t st) {
     switch (R) {
-    case 32: return project_bf16_r<32>(T, K, key, c, X, ldx, ws, st);
-    case 64: return project_bf16_r<64>(T, K, key, c, X, ldx, ws, st);
-    case 128: return project_bf16_r<128>(T, K, key, c, X, ldx, ws, st);
-    case 256: return project_bf16_r<256>(T, K, key, c, X, ldx, ws, st);
+    case 32: return project_bf16_r<32>(T, D, K, key, c, X, ldx, ws, st);
+    case 64: return project_bf16_r<64>(T, D, K, key, c, X, ldx, ws, st);
+    case 128: return project_bf16_r<128>(T, D, K, key, c, X, ldx, ws, st);
+    case 256: return project_bf16_r<256>(T, D, K, key, c, X, ldx, ws, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                            float *S, int accumulate, const void *ws, hipStream_t st) {
+                            float *S, int accumulate, void *ws, hipStream_t st) {
     switch (R) {
     case 32: return fold_bf16_r<32>(T, D, K, dY, lddy, S, accumulate, ws, st);
     case 64: return fold_bf16_r<64>(T, D, K, dY, lddy, S, accumulate, ws, st);

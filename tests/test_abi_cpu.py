@@ -98,11 +98,16 @@ def test_workspace_sizes(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
     m = B.MatrixDesc(18944, 3584, 256)
     ws = B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_BF16)
-    # the projected microbatch X A^T in bf16 (T x r); this d needs no split of the fold
-    assert ws == 4096 * 256 * 2
-    # a small d splits the fold over tokens: fp32 partial tiles follow P
+    # the projected microbatch X A^T in bf16 (T x r); then, for the two token
+    # halves that share each of the 128 tiles of up to 10 x 16 rows, their
+    # partial tiles as MFMA fragments (128 x 2 x 160 x r fp32) and their sync
+    # words (ticket counter, a flag per tile member, a counter per tile:
+    # 1 + 128 x 3 ints, rounded up to 256 bytes)
+    assert ws == 4096 * 256 * 2 + 128 * 2 * 160 * 256 * 4 + 1792
+    # a small d splits the tokens over more members (8 here), each writing a
+    # d x r fp32 partial for the reduction that follows
     small = B.logra_sketch_workspace_bytes(B.MatrixDesc(512, 3584, 256), 4096, B.LOGRA_BF16)
-    assert small > 4096 * 256 * 2 and (small - 4096 * 256 * 2) % (512 * 256 * 4) == 0
+    assert small == 4096 * 256 * 2 + 8 * 512 * 256 * 4
     assert B.logra_sketch_workspace_bytes(m, 0, B.LOGRA_BF16) == 0
     assert B.logra_sketch_workspace_bytes(m, 4096, B.LOGRA_F32) == 4096 * 256 * 4
     assert B.logra_sketch_workspace_bytes(B.MatrixDesc(64, 64, 48), 16, B.LOGRA_BF16) == 0

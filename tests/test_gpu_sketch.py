@@ -76,6 +76,60 @@ def test_sketch_bf16_matches_oracle(T, d, k, r, mbs):
     assert err < BF16_TOL
 
 
+# Work splits of the fold: tiles over two token halves that exchange partial
+# tiles (d >= 8192), more workgroups than compute units (d > 20480), tall
+# tiles over all tokens when T has fewer than 8 steps of 32 (two epilogue
+# passes), and small d with 8 members per tile; ragged T and d throughout.
+FOLD_SPLIT_CASES = [
+    # T, d, k, r, microbatches
+    (300, 8200, 136, 256, 2),
+    (4096, 512, 64, 256, 2),
+    (200, 41000, 72, 32, 2),
+    (257, 24008, 64, 64, 2),
+    (1000, 9000, 40, 128, 1),
+]
+
+
+@pytest.mark.parametrize("T,d,k,r,mbs", FOLD_SPLIT_CASES)
+def test_sketch_bf16_fold_splits(T, d, k, r, mbs):
+    dev = device()
+    say("sketch bf16 split", T, d, k, r, mbs)
+    m = B.MatrixDesc(d, k, r, seed=5, step=T, matrix_id=d)
+    X_list, dY_list = [], []
+    for n in range(mbs):
+        X, dY = inputs.random_case(2000 * T + n, T, d, k, dtype=torch.bfloat16, dy_std=1e-2,
+                                   outlier_cols=max(1, k // 100))
+        X_list.append(X)
+        dY_list.append(dY)
+    S = _run_sketch(m, X_list, dY_list, dev)
+    ref = _ref_sketch(m, X_list, dY_list)
+    err = rownorm_err(to_f64(S), ref)
+    say("  S rownorm err %.3e" % err)
+    assert err < BF16_TOL
+
+
+def test_fold_twice_from_one_projection():
+    # The fold leaves its sync words zero, so a second fold from the same
+    # projection and workspace is valid: it adds the same product again.
+    dev = device()
+    T, d, k, r = 320, 8208, 96, 256
+    m = B.MatrixDesc(d, k, r, 1, 2, 3)
+    X, dY = inputs.random_case(77, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    X, dY = X.to(dev), dY.to(dev)
+    ws = torch.empty(B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+    S = torch.empty(d, r, device=dev)
+    B.logra_sketch_project(m, X, ws)
+    B.logra_sketch_fold(m, dY, S, False, ws)
+    S1 = S.clone()
+    B.logra_sketch_fold(m, dY, S, True, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(S, 2 * S1)   # x + x is exact
+    S_acc = torch.empty(d, r, device=dev)
+    B.logra_sketch_accumulate(m, X, dY, S_acc, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(S_acc, S1)
+
+
 F32_CASES = [
     (128, 256, 512, 32, 4),     # the tiny fp32 workload's shape
     (77, 45, 130, 20, 2),
@@ -143,14 +197,18 @@ def test_accumulate_flag_and_linearity():
     assert torch.equal(S, S1)
 
 
-def test_deterministic_repeat():
+@pytest.mark.parametrize("T,d,k", [(700, 392, 1032), (600, 8200, 200)])
+def test_deterministic_repeat(T, d, k):
+    # bitwise repeatable, also where token halves exchange partial tiles and
+    # finish in whatever order
     dev = device()
-    T, d, k, r = 700, 392, 1032, 256
+    r = 256
     m = B.MatrixDesc(d, k, r, 4, 4, 4)
     X, dY = inputs.random_case(44, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
     a = _run_sketch(m, [X, X], [dY, dY], dev)
-    b = _run_sketch(m, [X, X], [dY, dY], dev)
-    assert torch.equal(a, b)
+    for _ in range(3):
+        b = _run_sketch(m, [X, X], [dY, dY], dev)
+        assert torch.equal(a, b)
 
 
 def test_empty_microbatch_and_zero_gradient():
