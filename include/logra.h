@@ -173,7 +173,9 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs
- * (per-block partial sums of the sqnorm reduction). 0 for invalid m.
+ * (per-block partial sums of the sqnorm reduction; on the bf16 path also the
+ * r x r Gram matrix of the signs and a counter that the call zeroes itself).
+ * 0 for invalid m. Calls that run at the same time need separate workspaces.
  */
 size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype);
 

@@ -33,7 +33,7 @@ float inv_sqrt_rank(int64_t r) { return 1.0f / sqrtf(static_cast<float>(r)); }
 size_t sqnorm_ws_bytes(const logra_matrix *m, int compute_dtype) {
     if (compute_dtype == LOGRA_BF16) {
         const SqnormPlan p = plan_sqnorm_bf16(m->d, m->k, static_cast<int>(m->r));
-        return p.partial_bytes + p.gram_bytes;
+        return p.partial_bytes + p.gram_bytes + p.counter_bytes;
     }
     return static_cast<size_t>(apply_blocks_f32(m->d)) * sizeof(float);
 }

@@ -28,10 +28,13 @@ namespace logra {
 // thread counts the sign differences of its pair.
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
-__global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M) {
+__global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
+                                                   int *__restrict__ counter) {
     __shared__ uint64_t wl[16][kGramChunk + 1];
     __shared__ uint64_t wm[16][kGramChunk + 1];
     const int tid = threadIdx.x;
+    // the rowsq kernel that follows counts its workgroups from zero
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *counter = 0;
     const int l0 = blockIdx.y * 16, m0 = blockIdx.x * 16;
     const int tl = tid >> 4, tm = tid & 15;
     const int nb = (K + 63) / 64;
@@ -61,128 +64,168 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
 }
 
 // rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
-// owns 128 rows of S, one wave 32 of them (two 16-row blocks i). M_off is
-// copied into LDS once per workgroup by direct global-to-LDS loads (no
-// registers), with the 16-byte chunks of row r stored in the order
-// chunk ^ (r mod 16), so a fragment's 16 rows fall on different banks.
-// The MFMA forms 16 x 16 blocks of Y^T with A = rows of M_off (LDS) and
-// B = S^T (bf16, registers). Row r = 4 q + e of block mb stands for
-// m = 32 (mb / 2) + 8 q + 4 (mb % 2) + e (M_off is symmetric, so any order of
-// m is a valid A operand), which puts in lane (n, g) exactly the Y[i][m] whose
-// S[i][m] it already holds in fp32 for its B fragment: the dot product and
-// the squares need no further loads.
+// owns bpw blocks of 16 rows of S (the plan makes about one workgroup per
+// compute unit) and stages them in LDS as fp32 (rows padded by 16 bytes, so
+// the 16 rows of a fragment fall on different banks). Each of the four waves
+// owns a quarter of the 16-row blocks of m and keeps their M_off fragments
+// (the MFMA A operand, straight from L2) in registers for the whole
+// workgroup, so M_off crosses each compute unit's memory path once and no
+// LDS copy of it is needed. Per row block the waves build the bf16 S^T
+// fragments (B operand) from LDS, form their 16 x 16 blocks of Y^T, and dot
+// each with the fp32 S entries of the same (i, m), also accumulating the
+// squares of those entries: every wave thus covers its m range of both sums,
+// and the four waves' partials are added per row in wave order. The
+// controller's sum ends in the same kernel: each workgroup stores its
+// partial with a device-coherent store, waits for it, and counts itself in;
+// the last one to arrive adds all partials in index order (fixed, so the
+// result does not depend on the arrival order) and clears the counter.
+constexpr int kRowsqMaxBlocks = 8;   // 16-row blocks of S per workgroup (most)
+constexpr int kRowsqWGs = 256;       // target workgroups (one per compute unit)
+
 template <int R>
 __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict__ S, int D, int K,
                                                          const uint16_t *__restrict__ M, float c,
                                                          const float *__restrict__ v, float beta2,
                                                          float eps, float *__restrict__ rowsq,
-                                                         float *__restrict__ partials) {
-    constexpr int KS = R / 32;                 // 32-wide steps of the rank
-    constexpr int NB = R / 16;                 // 16-row blocks of m
-    constexpr int CPR = R / 8;                 // 16-byte chunks per row of M_off
-    constexpr int SW = CPR < 16 ? CPR : 16;    // chunk swizzle period
-    __shared__ __attribute__((aligned(16))) uint16_t ms[R * R];
+                                                         float *__restrict__ partials, int bpw,
+                                                         int *__restrict__ counter, float *__restrict__ sqnorm) {
+    constexpr int KS = R / 32;                    // 32-wide steps of the rank
+    constexpr int NB = R / 16;                    // 16-row blocks of m
+    constexpr int MPW = NB >= 4 ? NB / 4 : 1;     // blocks of m per wave
+    constexpr int LD = R + 4;                     // fp32 stride of an S row in LDS
+    constexpr int CPR = R / 4;                    // 16-byte chunks per S row
+    constexpr int kMaxRows = kRowsqMaxBlocks * 16;
+    constexpr int kChunks = (kMaxRows * CPR + 255) / 256;   // staging chunks per thread (most)
+    __shared__ __attribute__((aligned(16))) float srow[kMaxRows * LD];
+    __shared__ float2 part[4][kMaxRows];          // per wave and row: (dot, squares)
     __shared__ float terms[4];
+    __shared__ float red[256];
+    __shared__ int last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int i0 = blockIdx.x * 128 + wave * 32;
+    const int r0 = blockIdx.x * bpw * 16;
+    const int rows = min(bpw * 16, D - r0);
+    const int mb0 = wave * MPW;
+    const bool active = mb0 < NB;                 // r = 32: two of the four waves have no m block
 
-    // This lane's S values, issued first: row i0 + 16 ib + n, columns
-    // 32 s + 8 g .. +7 (the B fragment before rounding, and the entries its
-    // Y values meet).
-    f32x4_t raw[2][KS][2];
+    // 1. this wave's M_off fragments: row m = 16 (mb0 + j) + n, k = 32 s + 8 g .. +7
+    u32x4_t mf[MPW][KS];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const float *srow = S + static_cast<int64_t>(min(i0 + 16 * ib + n, D - 1)) * R;   // rows past d are dropped
+    for (int j = 0; j < MPW; ++j)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            raw[ib][s][0] = *reinterpret_cast<const f32x4_t *>(srow + 32 * s + 8 * g);
-            raw[ib][s][1] = *reinterpret_cast<const f32x4_t *>(srow + 32 * s + 8 * g + 4);
+        for (int s = 0; s < KS; ++s)
+            mf[j][s] = active ? load_u32x4(M + static_cast<size_t>(16 * (mb0 + j) + n) * R + 32 * s + 8 * g)
+                              : zero_u32x4();
+    // 2. the workgroup's S rows into LDS, every load in flight before the stores (rows past d as zero)
+    {
+        f32x4_t st[kChunks];
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = tid + 256 * q, row = idx / CPR, ch = idx - row * CPR;
+            st[q] = row < rows ? *reinterpret_cast<const f32x4_t *>(S + static_cast<int64_t>(r0 + row) * R + 4 * ch)
+                               : zero_f32x4();
+        }
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+            const int idx = tid + 256 * q, row = idx / CPR, ch = idx - row * CPR;
+            if (row < bpw * 16) *reinterpret_cast<f32x4_t *>(&srow[row * LD + 4 * ch]) = st[q];
         }
     }
-    // stage M_off: each wave instruction moves 64 chunks; lane i's chunk
-    // lands at LDS chunk position q0 + i (row q / CPR, position q % CPR) and
-    // carries logical chunk position ^ (row mod SW)
-    for (int q0 = wave * 64; q0 < R * CPR; q0 += 256) {
-        const int q = q0 + lane;
-        const int row = q / CPR, pos = q - row * CPR;
-        const int ch = pos ^ (row & (SW - 1));
-        __builtin_amdgcn_global_load_lds(M + static_cast<size_t>(row) * R + 8 * ch,
-                                         (__attribute__((address_space(3))) void *)(ms + q0 * 8), 16, 0, 0);
-    }
-    u32x4_t bt[2][KS];
-    float ssq[2] = {0.f, 0.f};
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const f32x4_t lo = raw[ib][s][0], hi = raw[ib][s][1];
-            bt[ib][s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
-                                pack_bf16x2(hi.z, hi.w)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ssq[ib] = fmaf(hi[e], hi[e], fmaf(lo[e], lo[e], ssq[ib]));
-        }
     __syncthreads();
 
-    // A row n of block mb: m = 32 (mb / 2) + 8 (n / 4) + 4 (mb % 2) + n % 4
-    const int mrow_base = 8 * (n >> 2) + (n & 3);
-    float ydot[2] = {0.f, 0.f};
+    // 3. per row block: this wave's blocks of Y^T (lane (n, g) gets
+    // Y[i = 16 rb + n][m = 16 mb + 4 g + e]) dotted with S[i][m]
+    for (int rb = 0; rb < bpw; ++rb) {
+        const float *si = &srow[(16 * rb + n) * LD];
+        float yd = 0.f, sq = 0.f;
+        if (active) {
+            u32x4_t sb[KS];
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-        const int mrow = 32 * (mb >> 1) + 4 * (mb & 1) + mrow_base;
-        f32x4_t acc[2] = {zero_f32x4(), zero_f32x4()};
+            for (int s = 0; s < KS; ++s) {
+                const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(si + 32 * s + 8 * g);
+                const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(si + 32 * s + 8 * g + 4);
+                sb[s] = u32x4_t{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
+                                pack_bf16x2(hi.z, hi.w)};
+            }
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const u32x4_t af =
-                *reinterpret_cast<const u32x4_t *>(&ms[mrow * R + 8 * ((4 * s + g) ^ (mrow & (SW - 1)))]);
+            for (int j = 0; j < MPW; ++j) {
+                f32x4_t acc = zero_f32x4();
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) acc[ib] = mfma_bf16(af, bt[ib][s], acc[ib]);
+                for (int s = 0; s < KS; ++s) acc = mfma_bf16(mf[j][s], sb[s], acc);
+                const f32x4_t sv = *reinterpret_cast<const f32x4_t *>(si + 16 * (mb0 + j) + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    yd = fmaf(sv[e], acc[e], yd);
+                    sq = fmaf(sv[e], sv[e], sq);
+                }
+            }
         }
-        // lane (n, g) now holds Y[i][32 (mb / 2) + 8 g + 4 (mb % 2) + e]
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const f32x4_t sv = raw[ib][mb >> 1][mb & 1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ydot[ib] = fmaf(sv[e], acc[ib][e], ydot[ib]);
-        }
-    }
-    // add the four lanes of a row (g = 0..3), fixed butterfly order
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+        // the four lanes of a row (g = 0..3), fixed butterfly order
 #pragma unroll
         for (int off = 16; off < 64; off <<= 1) {
-            ydot[ib] += __shfl_xor(ydot[ib], off, 64);
-            ssq[ib] += __shfl_xor(ssq[ib], off, 64);
+            yd += __shfl_xor(yd, off, 64);
+            sq += __shfl_xor(sq, off, 64);
         }
-    // lanes g == ib write row i0 + 16 ib + n
+        if (g == 0) part[wave][16 * rb + n] = make_float2(yd, sq);
+    }
+    __syncthreads();
+
+    // 4. rowsq, v' and the controller's term, one thread per row
     float term = 0.f;
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const int i = i0 + 16 * ib + n;
-        if (g == ib && i < D) {
-            const float rq = (c * c) * fmaf(static_cast<float>(K), ssq[ib], ydot[ib]);
-            rowsq[i] = rq;
-            const float vn = beta2 * v[i] + (1.f - beta2) * (rq / static_cast<float>(K));
-            const float u = 1.f / (sqrtf(vn) + eps);
-            term += rq * u * u;
-        }
+    if (tid < rows) {
+        const float2 p0 = part[0][tid], p1 = part[1][tid], p2 = part[2][tid], p3 = part[3][tid];
+        const float yd = ((p0.x + p1.x) + p2.x) + p3.x;
+        const float sq = ((p0.y + p1.y) + p2.y) + p3.y;
+        const int i = r0 + tid;
+        const float rq = (c * c) * fmaf(static_cast<float>(K), sq, yd);
+        rowsq[i] = rq;
+        const float vn = beta2 * v[i] + (1.f - beta2) * (rq / static_cast<float>(K));
+        const float u = 1.f / (sqrtf(vn) + eps);
+        term = rq * u * u;
     }
     // per-workgroup partial of the controller's reduction, fixed order
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) term += __shfl_xor(term, off, 64);
     if (lane == 0) terms[wave] = term;
     __syncthreads();
-    if (tid == 0) partials[blockIdx.x] = ((terms[0] + terms[1]) + terms[2]) + terms[3];
+    if (tid == 0) {
+        const float pw = ((terms[0] + terms[1]) + terms[2]) + terms[3];
+        __hip_atomic_store(partials + blockIdx.x, pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is stored before the count
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = prev == static_cast<int>(gridDim.x) - 1;
+        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+    // sqnorm = the partials added in a fixed order: strided per thread, then a tree
+    float t = 0.f;
+    for (int i = tid; i < static_cast<int>(gridDim.x); i += 256)
+        t += __hip_atomic_load(partials + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    red[tid] = t;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) sqnorm[0] = red[0];
 }
 
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
     SqnormPlan p;
-    p.n_blocks = static_cast<int>((D + 127) / 128);
     (void)K;
+    (void)R;
+    const int64_t nblk = (D + 15) / 16;
+    int64_t bpw = (nblk + kRowsqWGs - 1) / kRowsqWGs;
+    if (bpw > kRowsqMaxBlocks) bpw = kRowsqMaxBlocks;
+    if (bpw < 1) bpw = 1;
+    p.rows_per_block = static_cast<int>(16 * bpw);
+    p.n_blocks = static_cast<int>((D + p.rows_per_block - 1) / p.rows_per_block);
     const size_t align = 256;
     p.partial_bytes = (static_cast<size_t>(p.n_blocks) * 4 + align - 1) / align * align;
     p.gram_bytes = (static_cast<size_t>(R) * R * 2 + align - 1) / align * align;
+    p.counter_bytes = align;
     return p;
 }
 
@@ -192,13 +235,13 @@ static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, hipStream_t st) {
     char *base = static_cast<char *>(ws);
     float *partials = reinterpret_cast<float *>(base);
     uint16_t *M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
+    int *counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
     const int K = static_cast<int>(a.K);
-    hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M);
+    hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter);
     hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
-                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.rowsq_out, partials);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_sqnorm_final(partials, p.n_blocks, a.sqnorm, st);
+                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.rowsq_out, partials,
+                       p.rows_per_block / 16, counter, a.sqnorm);
+    return hipGetLastError();
 }
 
 hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st) {

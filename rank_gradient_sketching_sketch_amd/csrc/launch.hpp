@@ -41,11 +41,15 @@ size_t workspace_sketch_f32(int64_t T, int64_t R);
 int apply_blocks_f32(int64_t D);
 
 // Workspace of apply pass 1 with bf16 compute: per-workgroup partials of the
-// controller's reduction, then the r x r Gram matrix of the signs (bf16).
+// controller's reduction, then the r x r Gram matrix of the signs (bf16),
+// then the counter the last workgroup is found with (zeroed by the Gram
+// kernel, left zero).
 struct SqnormPlan {
-    int n_blocks = 0;
+    int n_blocks = 0;         // workgroups of rowsq_gram_kernel
+    int rows_per_block = 0;   // rows of S each of them owns
     size_t partial_bytes = 0;
     size_t gram_bytes = 0;
+    size_t counter_bytes = 0;   // arrival counter of the last-workgroup reduction
 };
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R);
 
