@@ -8,9 +8,10 @@
 //
 // Work decomposition. The unit of work is one 256-row tile of W times one
 // 64-column tile; the units, in row-major order, are dealt to a fixed number
-// of workgroups as contiguous, equally sized ranges (one workgroup per
-// compute unit), so a workgroup touches at most a few row tiles and loads
-// their rows of S only once each. Neighbouring ranges (which share a row
+// of workgroups as contiguous ranges of equal cost, counting the load of a
+// row tile's S rows as a few units (one workgroup per compute unit), so a
+// workgroup touches at most a few row tiles and loads their rows of S only
+// once each. Neighbouring ranges (which share a row
 // tile) run on the same XCD, so S is fetched from HBM about once and the
 // other workgroups of the row tile find it in that XCD's L2. Eight waves
 // (two per SIMD, so one wave's vector work overlaps the other's matrix work)
@@ -65,8 +66,24 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // workgroup ids are dealt round-robin over the 8 XCDs
     const int G = gridDim.x;
     const int range = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : static_cast<int>(blockIdx.x);
-    const int u_begin = static_cast<int>((static_cast<int64_t>(range) * n_units) / G);
-    const int u_end = static_cast<int>((static_cast<int64_t>(range + 1) * n_units) / G);
+    // The ranges have equal cost rather than equal length: each row tile
+    // costs its n_ct units plus kTileCost more for loading its rows of S (the
+    // bytes of S per row tile over the bytes of W one unit reads and writes),
+    // so a range that starts a new row tile is that much shorter.
+    constexpr int kTileCost = (R * 4) / (kApplyCols * 2 * (WBF16 ? 2 : 4)) > 1
+                                  ? (R * 4) / (kApplyCols * 2 * (WBF16 ? 2 : 4))
+                                  : 1;
+    const int64_t per_tile = n_ct + kTileCost;
+    const int64_t total = static_cast<int64_t>(n_units / n_ct) * per_tile;
+    auto unit_at = [&](int64_t cpos) -> int {   // first unit at or after cost position cpos
+        const int64_t t = cpos / per_tile;
+        int64_t j = cpos - t * per_tile - kTileCost;
+        if (j < 0) j = 0;
+        const int64_t u = t * n_ct + j;
+        return static_cast<int>(u < n_units ? u : n_units);
+    };
+    const int u_begin = unit_at(static_cast<int64_t>(range) * total / G);
+    const int u_end = unit_at(static_cast<int64_t>(range + 1) * total / G);
 
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.W, 0, static_cast<int>(static_cast<int64_t>(D) * a.ldw * (WBF16 ? 2 : 4)), 0x00020000);
