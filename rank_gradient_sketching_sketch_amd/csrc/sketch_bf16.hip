@@ -20,7 +20,7 @@
 // into an LDS table (8 word blocks at a time), and every step expands one byte per lane into
 // eight bf16 +-1 values, the B operand of the MFMA. X streams straight from
 // HBM through buffer loads (rows past T and columns past k read as zero)
-// several steps ahead of use. The result is scaled by c, rounded to bf16
+// two steps ahead of use. The result is scaled by c, rounded to bf16
 // (nearest even) and written in the fold's operand layout
 // P[t / 32][l][t % 32], so a 16-byte load there is one MFMA fragment.
 #include "common.hpp"
@@ -32,7 +32,8 @@ namespace logra {
 constexpr int kS1Tokens = 32;     // tokens per workgroup (two 16-row MFMA blocks)
 constexpr int kS1Waves = 8;       // waves per workgroup; they split the k range
 constexpr int kS1Words = 8;       // sign-word blocks (64 columns of k each) hashed per refill
-constexpr int kS1Prefetch = 8;    // steps of X held in registers ahead of use
+constexpr int kS1Prefetch = 2;    // steps of X held in registers ahead of use (2 measured
+                                  // faster than 4 or 8: every CU requests its X at once)
 constexpr int kS1TileLd = 36;     // fp32 stride of one column of the reduction tile (32 + 4)
 
 template <int R>
