@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--workload", default="qwen7b_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=0,
-                    help="streams the matrices of a step are spread over (0: 1 for one matrix, else 3)")
+                    help="streams the matrices' sketch calls are spread over (0: at most 4)")
+    ap.add_argument("--apply-streams", type=int, default=0,
+                    help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -121,9 +123,15 @@ def main():
                       for s in wl.matrices)
     # Independent matrices run on separate streams (matrix i on stream i mod
     # n), each stream with its own workspaces, so small projections (k, v)
-    # overlap the large ones instead of leaving most of the GPU idle.
-    n_streams = args.streams or (1 if len(mats) == 1 else 3)
-    n_streams = max(1, min(n_streams, len(mats)))
+    # overlap the large ones instead of leaving most of the GPU idle. Four
+    # streams for the sketch phase (HIP gives a process four hardware queues
+    # by default; more streams share them and slowed the apply phase that
+    # follows), three for the apply phase, whose kernels fill the GPU longer.
+    n_sketch = args.streams or min(4, len(mats))
+    n_apply = args.apply_streams or (1 if len(mats) == 1 else 3)
+    n_sketch = max(1, min(n_sketch, len(mats)))
+    n_apply = max(1, min(n_apply, len(mats)))
+    n_streams = max(n_sketch, n_apply)
     main = torch.cuda.current_stream()
     lanes = []
     for i in range(n_streams):
@@ -133,7 +141,8 @@ def main():
             "sq_ws": torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev),
         })
     for i, m in enumerate(mats):
-        m["lane"] = lanes[i % n_streams]
+        m["lane"] = lanes[i % n_sketch]
+        m["alane"] = lanes[i % n_apply]
     # Microbatch buffers: every microbatch has its own; layer stacks rotate
     # two sets of per-layer inputs (even and odd layers), which keeps a
     # 28- or 64-layer step within memory while consecutive layers still read
@@ -212,7 +221,7 @@ def main():
         e1 = ev() if timed else None
         fork()
         for m in mats:
-            ln = m["lane"]
+            ln = m["alane"]
             B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["rowsq"],
                                   m["sq"], ln["sq_ws"], ln["stream"])
         join()
@@ -228,7 +237,7 @@ def main():
                 continue
             scale = inputs.step_scale(wl, m["spec"], step)
             B.logra_rowadam_apply(m["desc"], code, m["S"], m["v"], m["rowsq"], m["W"], wl.lr, scale,
-                                  wl.beta2, wl.eps, m["lane"]["stream"])
+                                  wl.beta2, wl.eps, m["alane"]["stream"])
         join()
         if timed:
             e4 = ev()
@@ -315,7 +324,7 @@ def main():
                    "microbatch_inputs": sum(t.numel() * t.element_size()
                                             for t in list(xbuf.values()) + list(ybuf.values())),
                    "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes))},
-        "streams": n_streams,
+        "streams": {"sketch": n_sketch, "apply": n_apply},
     }
 
     if not args.no_cpu_baseline:
