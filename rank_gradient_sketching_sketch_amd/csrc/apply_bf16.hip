@@ -27,7 +27,8 @@
 // 32 (cb / 2) + 8 (m / 4) + 4 (cb % 2) + m % 4, which puts 8 consecutive
 // columns of one row of W in each lane, so W moves in 16-byte vectors. W
 // goes through a buffer view (rows past d and columns past k read as zero
-// and are not written) and is requested two tiles ahead of its update.
+// and are not written) and is requested one tile ahead of its products (two
+// ahead of its update, which lags the products by one unit).
 //
 // Every workgroup of a row tile reads v and rowsq to form u_i; v itself is
 // committed by a separate small pass once all of them are done.
@@ -229,11 +230,10 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     p0.ct = u_begin - p0.rt * n_ct;
     Pos pp = p0;    // the unit whose update is written (one behind p0)
     pp.u = u_end;   // none yet: w_off masks every access of a unit >= u_end
-    const Pos p1 = advance(p0);
-    Pos p2 = advance(p1);   // the unit whose W and sign words are requested
-    u32x4_t wb[3][2][2][WV];   // W ring: slot (u - u_begin) % 3 holds unit u
+    Pos p1 = advance(p0);   // the unit whose W is requested
+    Pos p2 = advance(p1);   // the unit whose sign words are requested
+    u32x4_t wb[2][2][2][WV];   // W ring: slot (u - u_begin) % 2 holds unit u
     w_load(p0, wb[0]);
-    w_load(p1, wb[1]);
     hash_words(p0, 0);
     apply_lds_barrier();
     build_frags(0);
@@ -248,11 +248,11 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // Software pipeline, one unit per step: the products of unit u, the
     // update of unit u - 1 and the sign fragments of unit u + 1 share one
     // straight-line block, so the matrix cores and the vector units work at
-    // the same time. Units go in groups of three so the W ring index is a
+    // the same time. Units go in pairs so the W ring index (two slots) is a
     // compile-time constant.
-    for (int u0 = u_begin; u0 < u_end; u0 += 3) {
+    for (int u0 = u_begin; u0 < u_end; u0 += 2) {
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
+        for (int p = 0; p < 2; ++p) {
             const int u = u0 + p;
             if (u < u_end) {
                 const int buf = (u - u_begin) & 1;
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
                 float cf_cur[2];
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) cf_cur[rb] = coef_s[32 * wave + 16 * rb + n];
-                finish(prev, cf_prev, pp, wb[(p + 2) % 3]);   // unit u - 1 (slot (u - 1) % 3)
-                w_load(p2, wb[(p + 2) % 3]);                 // unit u + 2 into the freed slot
+                finish(prev, cf_prev, pp, wb[(p + 1) % 2]);   // unit u - 1 (slot (u - 1) % 2)
+                w_load(p1, wb[(p + 1) % 2]);                 // unit u + 1 into the freed slot
                 build_frags(buf ^ 1);
                 hash_words(p2, buf);
 #pragma unroll
@@ -290,16 +290,16 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
                 }
                 pp = p0;
                 p0 = advance(p0);
+                p1 = advance(p1);
                 p2 = advance(p2);
             }
         }
     }
     // the last unit's update: slot (u_end - 1 - u_begin) % 3
-    switch ((u_end - 1 - u_begin) % 3) {
-    case 0: finish(prev, cf_prev, pp, wb[0]); break;
-    case 1: finish(prev, cf_prev, pp, wb[1]); break;
-    default: finish(prev, cf_prev, pp, wb[2]); break;
-    }
+    if ((u_end - 1 - u_begin) % 2 == 0)
+        finish(prev, cf_prev, pp, wb[0]);
+    else
+        finish(prev, cf_prev, pp, wb[1]);
 }
 
 // v <- beta2 v + (1 - beta2) rowsq / k, after every workgroup of the apply has read v.
