@@ -51,6 +51,11 @@ APPLY_CASES = [
     (520, 1544, 256),
     (8, 8, 256),
     (1032, 4104, 256),
+    # pass 1 with 3 row blocks per workgroup and a ragged last workgroup
+    (8200, 136, 256),
+    # pass 1 with 258 workgroups of 8 row blocks: the last one to arrive adds
+    # more partials than it has threads
+    (33000, 72, 64),
 ]
 
 
