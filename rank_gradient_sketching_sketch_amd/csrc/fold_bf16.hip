@@ -171,6 +171,8 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     // wave and block, no staging); with more members, consecutive row ranges,
     // and the partials move as rows.
     constexpr int kHalf = Sh::HALF;
+    static_assert(MODE != kFoldPair || 16 * WM * (MBW - kHalf > kHalf ? MBW - kHalf : kHalf) <= kStage,
+                  "each member of a pair finalizes its rows in one staged pass");
     int own0, own1;
     if (MODE == kFoldPair) {
         own0 = mem == 0 ? 0 : min(16 * WM * kHalf, rows);
@@ -355,7 +357,14 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         return static_cast<uint32_t>(((((ti * 2 + q) * MAXB + mb) * Sh::WN + wn) * NBW + nb) * 1024 + lane * 16);
     };
 
+    // Old values of the rows a member of a pair finalizes (a single pass):
+    // requested before the exchange stores, so both drain together.
+    u32x4_t old_pre[kOutChunks];
     if (MODE == kFoldPair) {
+#pragma unroll
+        for (int c = 0; c < kOutChunks; ++c)
+            old_pre[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         s_rs, accumulate ? c_off(own0, own1, c) : kOob, 0, 0));
         // 1. this member's fragments of the blocks the other finalizes,
         // straight from the accumulators
 #pragma unroll
@@ -423,8 +432,10 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             u32x4_t old[kOutChunks];
 #pragma unroll
             for (int c = 0; c < kOutChunks; ++c)
-                old[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
+                old[c] = MODE == kFoldPair
+                             ? old_pre[c]
+                             : __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
 #pragma unroll
             for (int c = 0; c < kOutChunks; ++c) {
                 f32x4_t v = value(c);
