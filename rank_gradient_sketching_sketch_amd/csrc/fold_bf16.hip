@@ -37,9 +37,16 @@
 //     tickets from a counter when they start and a tile's two members hold
 //     consecutive tickets, so a member only ever waits for a workgroup that has
 //     already started: no co-residency beyond two workgroups is assumed.
+//     Workgroup ids are dealt round-robin over the 8 XCDs, so the ids of one
+//     residue mod 8 draw tickets from a counter of their own and cover
+//     consecutive tiles: a pair and its neighbouring tiles then normally share
+//     one L2. Each member publishes the XCD it runs on (hardware register
+//     XCC_ID); when both members are on one XCD the exchange stays in that
+//     L2 (plain stores, loads that bypass the L1), otherwise it uses
+//     device-coherent accesses, so the result never depends on placement.
 //     Waits are bounded; on time-out the rows are written as NaN rather than
-//     hanging. Stage 1 zeroes the counter and flags before each fold and the
-//     fold leaves them zero.
+//     hanging. Stage 1 zeroes the counters, flags and XCD words before each
+//     fold and the fold leaves them zero.
 //   * More members per tile (small d, so that the grid still fills the chip)
 //     each write their whole partial tile, and fold_reduce_kernel adds them in
 //     member order.
@@ -93,10 +100,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Cache policy of the exchange traffic: device scope (the SC1 bit, what
-// agent-scope atomic loads and stores compile to on gfx950), so a partial
-// written on one XCD is read correctly from another.
+// Cache policies of the exchange traffic. Between XCDs: device scope (the
+// SC1 bit, what agent-scope atomic loads and stores compile to on gfx950), so
+// a partial written on one XCD is read correctly from another. Within one
+// XCD the shared L2 is the point of coherence: plain stores (the vector L1
+// writes through) and loads that bypass the L1 (SC0, workgroup scope).
 constexpr int kDeviceScope = 16;
+constexpr int kL1Bypass = 1;
+// s_getreg operand of HW_REG_XCC_ID (register 20, bits 0..3): the XCD a wave runs on.
+constexpr int kHwRegXccId = 20 | (0 << 6) | (3 << 11);
 
 // How the members of a tile add their partials: one member (nothing to
 // add); two, exchanging MFMA fragments within the kernel; or more, each
@@ -131,6 +143,11 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const int i16 = lane & 15, g = lane >> 4;
     const int G = n_tiles * n_split;
 
+    // Sync words of the pair mode: the ticket counter, one counter per id
+    // group, each member's flag, each tile's done count, each member's XCD.
+    int *flags = sync + 1 + kXcds;
+    int *done = flags + G;
+    int *xcd_of = done + n_tiles;
     // Tile and member: a ticket when members exchange partials; otherwise
     // the workgroup id, with consecutive tiles on one XCD (ids are dealt
     // round-robin over the XCDs) so the cache lines that neighbouring tiles
@@ -138,12 +155,25 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     int ticket;
     if (MODE == kFoldPair) {
         if (tid == 0) {
+            // With G a multiple of 16, the ids of one group (id mod 8, the
+            // XCD they are dealt to) draw tickets among themselves and hold
+            // consecutive tiles, so a tile's two members and its neighbours
+            // normally share an XCD; otherwise one counter for all.
+            const bool grouped = G % (2 * kXcds) == 0;
+            const int grp = static_cast<int>(blockIdx.x % kXcds);
+            int *ctr = grouped ? sync + 1 + grp : sync;
+            const int n = grouped ? G / kXcds : G;
             const unsigned t = static_cast<unsigned>(
-                __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
             // in range even if the counter was not zeroed (no projection made
             // in this workspace): then the results are undefined, not a fault
-            const int tk = static_cast<int>(t % static_cast<unsigned>(G));
-            if (tk == G - 1) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int lt = static_cast<int>(t % static_cast<unsigned>(n));
+            if (lt == n - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int tk = grouped ? grp * n + lt : lt;
+            // the XCD this workgroup runs on (hardware register), published
+            // for the partner as id + 1
+            const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u);
+            __hip_atomic_store(xcd_of + tk, xcd + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_word = tk;
         }
         __syncthreads();
@@ -347,8 +377,6 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         return (row < r1 && d0 + row < D) ? s_off(row, chunk_col(c)) : kOob;
     };
 
-    int *flags = sync + 1;
-    int *done = flags + n_tiles * n_split;
     const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(xbuf, 0, x_bytes, 0x00020000);
     const uint32_t x_stride = static_cast<uint32_t>(static_cast<int64_t>(D) * R * 4);   // rows layout
     // fragment (member q, row block mb, column block nb of this wave) in the
@@ -360,11 +388,27 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
     // Old values of the rows a member of a pair finalizes (a single pass):
     // requested before the exchange stores, so both drain together.
     u32x4_t old_pre[kOutChunks];
+    bool same_xcd = false;   // the pair's exchange stays in one L2
     if (MODE == kFoldPair) {
 #pragma unroll
         for (int c = 0; c < kOutChunks; ++c)
             old_pre[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                          s_rs, accumulate ? c_off(own0, own1, c) : kOob, 0, 0));
+        // whether the other member runs on this XCD (it has published its
+        // XCD since it started; a bounded wait, as for its flag below)
+        if (tid == 0) {
+            const int mine = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u) + 1;
+            int other = 0;
+            for (int spins = 0; spins <= kFoldSpinLimit; ++spins) {
+                other = __hip_atomic_load(xcd_of + ti * n_split + (1 - mem), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (other != 0) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            s_word = other == mine;
+        }
+        __syncthreads();
+        same_xcd = s_word != 0;
         // 1. this member's fragments of the blocks the other finalizes,
         // straight from the accumulators
 #pragma unroll
@@ -372,9 +416,13 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
             const int mb = wm + j * WM;
             if (mb < nmb && (j < kHalf) == (mem == 1)) {
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[j][nb]), x_rs,
-                                                          x_frag(mem, mb, nb), 0, kDeviceScope);
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const u32x4_t v = __builtin_bit_cast(u32x4_t, acc[j][nb]);
+                    if (same_xcd)
+                        __builtin_amdgcn_raw_buffer_store_b128(v, x_rs, x_frag(mem, mb, nb), 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(v, x_rs, x_frag(mem, mb, nb), 0, kDeviceScope);
+                }
             }
         }
     } else if (MODE == kFoldPartial) {
@@ -456,10 +504,12 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
                 for (int j = J0; j < J1; ++j) {
                     const int mb = wm + j * WM;
 #pragma unroll
-                    for (int nb = 0; nb < NBW; ++nb)
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const uint32_t off = mb < nmb ? x_frag(1 - mem, mb, nb) : kOob;
                         x[j - J0][nb] = __builtin_bit_cast(
-                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                         x_rs, mb < nmb ? x_frag(1 - mem, mb, nb) : kOob, 0, kDeviceScope));
+                            f32x4_t, same_xcd ? __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, kL1Bypass)
+                                              : __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, kDeviceScope));
+                    }
                 }
                 // stage the own rows (all of blocks J0 .. J1 - 1) as acc + x
                 lds_barrier();   // the previous user of the LDS is done
@@ -497,8 +547,10 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         if (tid == 0) {
             const int prev = __hip_atomic_fetch_add(done + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (prev == n_split - 1) {
-                for (int q = 0; q < n_split; ++q)
+                for (int q = 0; q < n_split; ++q) {
                     __hip_atomic_store(flags + ti * n_split + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(xcd_of + ti * n_split + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 __hip_atomic_store(done + ti, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -555,7 +607,9 @@ FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R) {
     if (p.n_split == 2) {
         // fragments of every block of every tile, then the sync words
         p.xbuf_bytes = (static_cast<size_t>(p.n_tiles) * 2 * p.max_blocks * 16 * R * 4 + align - 1) / align * align;
-        p.sync_words = 1 + p.n_tiles * p.n_split + p.n_tiles;
+        // ticket counter, one counter per id group, a flag and an XCD per
+        // member, a done count per tile
+        p.sync_words = 1 + kXcds + 2 * p.n_tiles * p.n_split + p.n_tiles;
         p.sync_bytes = (static_cast<size_t>(p.sync_words) * 4 + align - 1) / align * align;
     } else if (p.n_split > 2) {
         // one d x r partial per member

@@ -101,9 +101,10 @@ def test_workspace_sizes(lib):
     # the projected microbatch X A^T in bf16 (T x r); then, for the two token
     # halves that share each of the 128 tiles of up to 10 x 16 rows, their
     # partial tiles as MFMA fragments (128 x 2 x 160 x r fp32) and their sync
-    # words (ticket counter, a flag per tile member, a counter per tile:
-    # 1 + 128 x 3 ints, rounded up to 256 bytes)
-    assert ws == 4096 * 256 * 2 + 128 * 2 * 160 * 256 * 4 + 1792
+    # words (ticket counter, one counter per workgroup-id group of the 8 XCDs,
+    # a flag and an XCD id per tile member, a counter per tile:
+    # 1 + 8 + 128 x 5 ints = 2596 bytes, rounded up to 256 bytes)
+    assert ws == 4096 * 256 * 2 + 128 * 2 * 160 * 256 * 4 + 2816
     # a small d splits the tokens over more members (8 here), each writing a
     # d x r fp32 partial for the reduction that follows
     small = B.logra_sketch_workspace_bytes(B.MatrixDesc(512, 3584, 256), 4096, B.LOGRA_BF16)
