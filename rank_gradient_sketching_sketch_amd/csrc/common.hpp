@@ -44,15 +44,25 @@ __device__ __forceinline__ uint32_t join_hi16(uint32_t lo, uint32_t hi) {
 
 // Eight sign bits x (bit e = sign of element e, 1 means -1) -> eight bf16
 // +-1.0 values (0x3F80 / 0xBF80) in four dwords, element 2q in the low half
-// of dword q. Only the low 8 bits of x may be set.
-__device__ __forceinline__ u32x4_t signs8_to_bf16(uint32_t x) {
+// of dword q. Only the low 8 bits of x may be set. `one` must hold 0x3F803F80
+// in a register (see opaque_u32): then each dword is a shift and one
+// v_and_or_b32, since a gfx9 VOP3 instruction takes no literal operand and
+// with both constants as literals the compiler emits shift, and, or.
+__device__ __forceinline__ u32x4_t signs8_to_bf16(uint32_t x, uint32_t one) {
     const uint32_t y = x | (x << 15);   // bit i at i and at i + 15
     u32x4_t r;
-    r.x = ((y << 15) & 0x80008000u) | 0x3F803F80u;
-    r.y = ((y << 13) & 0x80008000u) | 0x3F803F80u;
-    r.z = ((y << 11) & 0x80008000u) | 0x3F803F80u;
-    r.w = ((y << 9) & 0x80008000u) | 0x3F803F80u;
+    r.x = ((y << 15) & 0x80008000u) | one;
+    r.y = ((y << 13) & 0x80008000u) | one;
+    r.z = ((y << 11) & 0x80008000u) | one;
+    r.w = ((y << 9) & 0x80008000u) | one;
     return r;
+}
+
+// A constant in a vector register that the compiler cannot fold back into
+// the instructions that use it (an empty asm statement owns it once).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 __device__ __forceinline__ u32x4_t zero_u32x4() { return u32x4_t{0u, 0u, 0u, 0u}; }

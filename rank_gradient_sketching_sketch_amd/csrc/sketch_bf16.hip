@@ -118,6 +118,7 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) xa[p][mb] = xload(s_begin + p, mb);
 
+    const uint32_t one_pair = opaque_u32(0x3F803F80u);   // two bf16 +1.0
     int first = kb0;   // first block held in the table
     if (s_begin < s_end) refill(first);
     // Whole groups of PF steps; steps past s_end load zeros and their
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
                 for (int nb = 0; nb < NB; ++nb) {
                     const uint64_t w = wrow[16 * nb];
                     const uint32_t dw = (s & 1) ? static_cast<uint32_t>(w >> 32) : static_cast<uint32_t>(w);
-                    bf[nb] = signs8_to_bf16(__builtin_amdgcn_ubfe(dw, 8 * g, 8));
+                    bf[nb] = signs8_to_bf16(__builtin_amdgcn_ubfe(dw, 8 * g, 8), one_pair);
                 }
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
