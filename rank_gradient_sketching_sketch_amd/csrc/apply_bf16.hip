@@ -43,6 +43,7 @@ constexpr int kApplyRows = 256;        // rows of W per row tile (32 per wave)
 constexpr int kApplyWaves = 8;
 constexpr int kApplyCols = 64;         // columns per column tile (one sign word)
 constexpr int kApplyWGs = 256;         // workgroups (one per compute unit)
+constexpr int kStagePitch = 144;       // bytes per staged row of a wave's updated bf16 block
 
 // Barrier that orders LDS traffic only (global loads stay in flight).
 __device__ __forceinline__ void apply_lds_barrier() {
@@ -59,6 +60,10 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     __shared__ uint32_t words[2][2][R];        // [buffer][half of the 64 columns][l]
     __shared__ __attribute__((aligned(16))) u32x4_t frags[2][NF][64];   // [buffer][fragment][lane]
     __shared__ float coef_s[kApplyRows];
+    // bf16 W: each wave's updated 32 x 64 block on its way from the MFMA
+    // layout to whole-line stores (rows padded to 144 bytes: conflict-free
+    // both ways)
+    __shared__ __attribute__((aligned(16))) uint8_t wstage[WBF16 ? kApplyWaves * 32 * kStagePitch : 16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -194,22 +199,55 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // holds row 32 wave + 16 rb + n, columns 32 (cb / 2) + 8 g + 4 (cb % 2) .. +3.
     auto finish = [&](const f32x4_t (&acc)[2][4], const float (&cf)[2], const Pos &p,
                       const u32x4_t (&wv)[2][2][WV]) {
+        if (WBF16) {
+            // The MFMA layout gives each lane 16 bytes of one row, so a wave's
+            // store would cover 16 rows x 64 bytes (half cache lines). The
+            // wave writes its block to LDS instead and stores it back as 8
+            // rows x 128 bytes per instruction (lane L: row 8 q + L / 8,
+            // columns 8 (L % 8) .. +7), whole lines, which HBM takes much
+            // faster.
+            uint8_t *blk = wstage + wave * 32 * kStagePitch;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
-                const uint32_t off = w_off(p, rb, h);
-                const float c = cf[rb];
-                if (WBF16) {
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
+                    const float c = cf[rb];
                     const u32x4_t w = wv[rb][h][0];
                     u32x4_t o;
                     o.x = pack_bf16x2(fmaf(-c, x0.x, bf16_lo(w.x)), fmaf(-c, x0.y, bf16_hi(w.x)));
                     o.y = pack_bf16x2(fmaf(-c, x0.z, bf16_lo(w.y)), fmaf(-c, x0.w, bf16_hi(w.y)));
                     o.z = pack_bf16x2(fmaf(-c, x1.x, bf16_lo(w.z)), fmaf(-c, x1.y, bf16_hi(w.z)));
                     o.w = pack_bf16x2(fmaf(-c, x1.z, bf16_lo(w.w)), fmaf(-c, x1.w, bf16_hi(w.w)));
-                    __builtin_amdgcn_raw_buffer_store_b128(o, w_rs, off, 0, 0);
-                } else {
+                    *reinterpret_cast<u32x4_t *>(blk + (16 * rb + n) * kStagePitch + 64 * h + 16 * g) = o;
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            const int lr = lane >> 3, lc = lane & 7;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = 8 * q + lr;
+                const u32x4_t o = *reinterpret_cast<const u32x4_t *>(blk + row * kStagePitch + 16 * lc);
+                const int i = p.rt * kApplyRows + 32 * wave + row;
+                const int jc = p.ct * kApplyCols + 8 * lc;
+                const uint32_t off = (p.u < u_end && i < D && jc < K)
+                                         ? static_cast<uint32_t>((static_cast<int64_t>(i) * a.ldw + jc) * 2)
+                                         : kOobOff;
+                __builtin_amdgcn_raw_buffer_store_b128(o, w_rs, off, 0, 0);
+            }
+            // the reads above are done before the next unit's block is written
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
+                    const uint32_t off = w_off(p, rb, h);
+                    const float c = cf[rb];
                     f32x4_t w0v = __builtin_bit_cast(f32x4_t, wv[rb][h][0]);
                     f32x4_t w1v = __builtin_bit_cast(f32x4_t, wv[rb][h][WV - 1]);
                     w0v.x = fmaf(-c, x0.x, w0v.x); w0v.y = fmaf(-c, x0.y, w0v.y);
@@ -220,7 +258,7 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w1v), w_rs,
                                                           off == kOobOff ? off : off + 16, 0, 0);
                 }
-            }
+        }
     };
 
     if (u_begin >= u_end) return;
