@@ -21,11 +21,14 @@
 
 namespace logra {
 
-// M_off[l][m] (bf16, row-major r x r, zero diagonal) = k - 2 popcount(sigma_l
-// xor sigma_m). A workgroup owns a 16 x 16 tile of (l, m); the sign words of
-// its 32 rows are hashed into LDS 64 blocks at a time (rows padded by one
-// word so the 16 rows of a column read fall on different banks) and each
-// thread counts the sign differences of its pair.
+// M_off[l][m] (bf16, zero diagonal) = k - 2 popcount(sigma_l xor sigma_m),
+// stored in MFMA operand order: the fragment of 16-row block lb and 32-wide
+// step s of m is 1 KB, lane (n, g) holding M_off[16 lb + n][32 s + 8 g .. +7]
+// in 16 bytes, so a wave loads one fragment as one contiguous kilobyte. A
+// workgroup owns a 16 x 16 tile of (l, m); the sign words of its 32 rows are
+// hashed into LDS 64 blocks at a time (rows padded by one word so the 16 rows
+// of a column read fall on different banks) and each thread counts the sign
+// differences of its pair.
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
 __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
@@ -60,7 +63,9 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
     }
     const int l = l0 + tl, m = m0 + tm;
     const float v = l == m ? 0.f : static_cast<float>(K - 2 * pc);
-    M[static_cast<size_t>(l) * R + m] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    const int frag = (l >> 4) * (R / 32) + (m >> 5);
+    const int ln = (((m & 31) >> 3) << 4) | (l & 15);   // lane (n = l % 16, g = (m % 32) / 8)
+    M[(static_cast<size_t>(frag) * 64 + ln) * 8 + (m & 7)] = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 // rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
@@ -110,12 +115,13 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
     const bool active = mb0 < NB;                 // r = 32: two of the four waves have no m block
 
     // 1. this wave's M_off fragments: row m = 16 (mb0 + j) + n, k = 32 s + 8 g .. +7
+    // (fragment order: one contiguous kilobyte per fragment)
     u32x4_t mf[MPW][KS];
 #pragma unroll
     for (int j = 0; j < MPW; ++j)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            mf[j][s] = active ? load_u32x4(M + static_cast<size_t>(16 * (mb0 + j) + n) * R + 32 * s + 8 * g)
+            mf[j][s] = active ? load_u32x4(M + (static_cast<size_t>((mb0 + j) * KS + s) * 64 + lane) * 8)
                               : zero_u32x4();
     // 2. the workgroup's S rows into LDS, every load in flight before the stores (rows past d as zero)
     {
