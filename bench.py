@@ -37,7 +37,7 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # + WRITE_SIZE x 1, the factors a plain device copy gives), per workload; see
 # profiles/hbm_traffic_qwen7b_up.md. Only valid for the fold kernel as it was
 # when the counters were taken.
-FOLD_TRAFFIC_BYTES = {"qwen7b_up": (107793 * 2 + 37924) * 1024}
+FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102541 * 2 + 37940) * 1024}
 
 
 def parse():
