@@ -38,6 +38,11 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # profiles/hbm_traffic_qwen7b_up.md. Only valid for the fold kernel as it was
 # when the counters were taken.
 FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102541 * 2 + 37940) * 1024}
+# Predicted-KL controller run on every step's sqnorms and reported: an
+# isotropic Fisher of scale 1 and a budget annealed from 1e-3 to 1e-4 nats
+# over 1000 steps (the pages give no values). The update itself uses the
+# workload's drawn scale.
+KL_PHI = 1.0
 
 
 def parse():
@@ -100,6 +105,7 @@ def main():
         from rank_gradient_sketching_sketch_amd import build_lib
         build_lib.build()
     B.load_library()
+    kl_budget = B.KLBudget(1e-3, 1e-4, 1000)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = inputs.WORKLOADS[args.workload]
@@ -226,9 +232,13 @@ def main():
                                   m["sq"], ln["sq_ws"], ln["stream"])
         join()
         e2 = ev() if timed else None
-        # step controller stand-in: read every sqnorm, skip non-finite ones,
-        # use the drawn scale (the controller's formula is not part of this path)
+        # one device->host read of every sqnorm; the library's host controller
+        # predicts the step's KL from them (reported, and timed on the host);
+        # the update uses the workload's drawn scale, skipping non-finite ones
         sqs = torch.cat([m["sq"] for m in mats]).cpu().tolist()
+        c0 = time.perf_counter()
+        gamma, kl_pred, _ = B.logra_kl_step_scale(sqs, wl.lr, KL_PHI, B.logra_kl_budget_at(kl_budget, step))
+        ctl_log.append((time.perf_counter() - c0, kl_pred, float(gamma.max()) if len(gamma) else 1.0))
         e3 = ev() if timed else None
         fork()
         for m, sq in zip(mats, sqs):
@@ -245,6 +255,7 @@ def main():
             ev_log.append(("sqnorm", e1, e2))
             ev_log.append(("apply", e3, e4))
 
+    ctl_log = []
     for s in range(args.warmup):
         one_step(s, False)
     torch.cuda.synchronize()
@@ -325,6 +336,11 @@ def main():
                                             for t in list(xbuf.values()) + list(ybuf.values())),
                    "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes))},
         "streams": {"sketch": n_sketch, "apply": n_apply},
+        "controller": {"fisher_scale": KL_PHI,
+                       "budget": [kl_budget.delta_start, kl_budget.delta_end, kl_budget.anneal_steps],
+                       "kl_pred_last_step": ctl_log[-1][1], "gamma_last_step": ctl_log[-1][2],
+                       "host_us_per_step": round(1e6 * sum(c[0] for c in ctl_log) / len(ctl_log), 2),
+                       "applied": False},
     }
 
     if not args.no_cpu_baseline:

@@ -23,7 +23,8 @@
  *        (sqrt(v'_i) + eps). RowAdam keeps one second moment per row and no
  *        first moment.
  *   A host-side step controller reads sqnorm between the two passes and
- *   picks scale; the controller is not part of this library.
+ *   picks scale. One is provided (logra_kl_step_scale, host code at the end
+ *   of this header); a caller may use any other.
  *
  * Sign hash (fixed so that any implementation reproduces A bit for bit):
  *   mix(z)   : SplitMix64 finaliser, z ^= z>>30; z *= 0xBF58476D1CE4E5B9;
@@ -34,7 +35,8 @@
  *   Sigma[l][j] = -1 if bit (j mod 64) of word(l, j/64) is 1, else +1.
  *
  * Conventions for every entry point:
- *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *   - All data pointers are DEVICE pointers owned by the caller (except the
+ *     host arrays of the step controller at the end). The library
  *     allocates nothing, keeps no mutable global state and is reentrant.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; results are visible after the caller
@@ -230,6 +232,60 @@ logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype,
                                  void *W, int w_dtype, int64_t ldw,
                                  float lr, float scale, float beta2, float eps,
                                  void *stream);
+
+/*
+ * Predicted-KL step control (host side; no device work).
+ *
+ * Before each update the step is scaled so that the predicted change of the
+ * policy stays within a KL budget that is annealed over training ("LoGRA:
+ * Scaling LLM Reinforcement Learning...", paragraph "Step control."; the KL
+ * is predicted from the sketch itself: "NVIDIA's LoGRA fits RL
+ * post-training...", section "Why it matters"; the shrink factor is closed
+ * form and applied when the prediction exceeds the budget: the walk-through
+ * page on LoGRA, section "Predicted-KL Step Control"). The pages do not give
+ * the Fisher weighting or the schedule; the readings taken here:
+ *   - local quadratic model with an isotropic Fisher, F = phi I:
+ *       KL(dW) = 0.5 * phi * sum over matrices of ||dW||_F^2, and with the
+ *       RowAdam update dW = -lr * Ghat / (sqrt(v') + eps) that is
+ *       KL = 0.5 * phi * lr^2 * sum_m sqnorm_m  (sqnorm from
+ *       logra_update_sqnorm), so KL(gamma dW) = gamma^2 KL(dW);
+ *   - one shrink factor per step, gamma = min(1, sqrt(delta_t / KL));
+ *   - delta_t annealed linearly from delta_start to delta_end over
+ *     anneal_steps steps, constant afterwards.
+ */
+typedef struct logra_kl_budget {
+    double delta_start;     /* budget at step 0 (>= 0, finite)                  */
+    double delta_end;       /* budget from step anneal_steps on (>= 0, finite)  */
+    uint64_t anneal_steps;  /* length of the linear anneal; 0: delta_end always */
+} logra_kl_budget;
+
+/*
+ * logra_kl_budget_at -- delta_t = delta_start + (delta_end - delta_start) *
+ * step / anneal_steps for step < anneal_steps, delta_end from then on (and
+ * always when anneal_steps == 0).
+ * Returns NaN for b == NULL or a negative or non-finite budget.
+ */
+double logra_kl_budget_at(const logra_kl_budget *b, uint64_t step);
+
+/*
+ * logra_kl_step_scale -- the step controller's decision for one step.
+ *   sqnorm   n host floats, the per-matrix sqnorm of logra_update_sqnorm
+ *            (copied to the host). Entries that are negative or not finite
+ *            are left out of the prediction and get scale 0 (no update).
+ *   lr       the step's learning rate (finite).
+ *   fisher_scale  phi > 0 (finite), the isotropic Fisher stand-in.
+ *   delta    the budget of this step (>= 0, finite; see logra_kl_budget_at).
+ *   scales   n host floats, out: gamma for every kept matrix, 0 otherwise.
+ *   kl_pred  host, out: 0.5 * phi * lr^2 * (sum of the kept sqnorm, in
+ *            index order, in double).
+ *   kl_after host, out (may be NULL): gamma^2 * kl_pred.
+ * gamma = 1 when kl_pred <= delta, else sqrt(delta / kl_pred).
+ * Errors: INVALID_ARGUMENT for n < 0, NULL sqnorm/scales with n > 0, NULL
+ *   kl_pred, or lr, fisher_scale, delta outside the ranges above. Nothing is
+ *   written on error.
+ */
+logra_status logra_kl_step_scale(const float *sqnorm, int64_t n, float lr, double fisher_scale,
+                                 double delta, float *scales, double *kl_pred, double *kl_after);
 
 #ifdef __cplusplus
 }

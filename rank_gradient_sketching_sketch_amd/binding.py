@@ -39,6 +39,16 @@ class MatrixDesc(ctypes.Structure):
         super().__init__(int(d), int(k), int(r), int(seed), int(step), int(matrix_id))
 
 
+class KLBudget(ctypes.Structure):
+    """logra_kl_budget: KL budget annealed linearly from delta_start to
+    delta_end over anneal_steps steps."""
+    _fields_ = [("delta_start", ctypes.c_double), ("delta_end", ctypes.c_double),
+                ("anneal_steps", ctypes.c_uint64)]
+
+    def __init__(self, delta_start, delta_end, anneal_steps=0):
+        super().__init__(float(delta_start), float(delta_end), int(anneal_steps))
+
+
 _lib = None
 
 
@@ -76,6 +86,11 @@ def load_library():
     lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
     lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, P, i32, i64, f32, f32, f32, f32, P]
+    dbl = ctypes.c_double
+    lib.logra_kl_budget_at.restype = dbl
+    lib.logra_kl_budget_at.argtypes = [ctypes.POINTER(KLBudget), u64]
+    lib.logra_kl_step_scale.restype = i32
+    lib.logra_kl_step_scale.argtypes = [P, i64, f32, dbl, dbl, P, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
     _lib = lib
     return lib
 
@@ -187,3 +202,22 @@ def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: t
         ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), _ptr(rowsq), _ptr(W),
         _dtype_code(W), _ld(W), float(lr), float(scale), float(beta2), float(eps),
         _stream(stream)), "logra_rowadam_apply")
+
+
+def logra_kl_budget_at(budget: KLBudget, step: int) -> float:
+    """The annealed KL budget of optimizer step `step` (host)."""
+    return float(load_library().logra_kl_budget_at(ctypes.byref(budget), int(step)))
+
+
+def logra_kl_step_scale(sqnorm, lr: float, fisher_scale: float, delta: float):
+    """Host step controller. sqnorm: sequence or array of per-matrix sqnorms.
+    Returns (scales as a float32 numpy array, kl_pred, kl_after)."""
+    import numpy as np
+    q = np.ascontiguousarray(np.asarray(sqnorm, dtype=np.float32).reshape(-1))
+    out = np.zeros(q.size, dtype=np.float32)
+    kl_pred, kl_after = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(load_library().logra_kl_step_scale(
+        q.ctypes.data_as(ctypes.c_void_p), q.size, float(lr), float(fisher_scale), float(delta),
+        out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(kl_pred), ctypes.byref(kl_after)),
+        "logra_kl_step_scale")
+    return out, kl_pred.value, kl_after.value
