@@ -120,7 +120,7 @@ def main():
             "S": torch.empty(spec.d, r, dtype=torch.float32, device=dev),
             "v": inputs.second_moment(wl, spec, device=dev),
             "W": inputs.weights(wl, spec, device=dev),
-            "rowsq": torch.empty(spec.d, dtype=torch.float32, device=dev),
+            "v_new": torch.empty(spec.d, dtype=torch.float32, device=dev),
             "sq": torch.empty(1, dtype=torch.float32, device=dev),
         })
     ws_bytes = max(B.logra_sketch_workspace_bytes(B.MatrixDesc(s.d, s.k, r), T, code)
@@ -188,7 +188,8 @@ def main():
         for mb in range(nmb):
             fold_bytes_per_step += 2.0 * T * s.d + 2.0 * T * r + 4.0 * s.d * r * (2 if mb > 0 else 1)
     wbytes = 2 if wl.w_dtype == torch.bfloat16 else 4
-    apply_bytes_per_step = sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * r + 8.0 * s.d + 8.0 * s.d
+    # W read and written, S read once, v read, v' written (pass 1) and read (pass 2)
+    apply_bytes_per_step = sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * r + 12.0 * s.d
                                for s in wl.matrices)
 
     # Event records cost a few microseconds of GPU time each, so the timed
@@ -228,8 +229,8 @@ def main():
         fork()
         for m in mats:
             ln = m["alane"]
-            B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["rowsq"],
-                                  m["sq"], ln["sq_ws"], ln["stream"])
+            B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
+                                  m["sq"], None, ln["sq_ws"], ln["stream"])
         join()
         e2 = ev() if timed else None
         # one device->host read of every sqnorm; the library's host controller
@@ -246,8 +247,10 @@ def main():
                 skipped[0] += 1
                 continue
             scale = inputs.step_scale(wl, m["spec"], step)
-            B.logra_rowadam_apply(m["desc"], code, m["S"], m["v"], m["rowsq"], m["W"], wl.lr, scale,
-                                  wl.beta2, wl.eps, m["alane"]["stream"])
+            B.logra_rowadam_apply(m["desc"], code, m["S"], m["v_new"], m["W"], wl.lr, scale, wl.eps,
+                                  m["alane"]["stream"])
+            # the update is applied: v' becomes the next step's v (buffer swap)
+            m["v"], m["v_new"] = m["v_new"], m["v"]
         join()
         if timed:
             e4 = ev()

@@ -16,12 +16,15 @@
  *   within it; it is never stored: every kernel regenerates the signs it
  *   needs from a counter hash of (seed, step, matrix_id). At update time the
  *   estimate Ghat = S A is rebuilt tile by tile, twice:
- *     pass 1 (logra_update_sqnorm): rowsq_i = sum_j Ghat_ij^2 and the
- *        controller's reduction sqnorm = sum_ij (Ghat_ij / (sqrt(v'_i)+eps))^2
- *        with v'_i = beta2 v_i + (1 - beta2) rowsq_i / k;
- *     pass 2 (logra_rowadam_apply): v <- v', W_ij -= lr*scale*Ghat_ij /
- *        (sqrt(v'_i) + eps). RowAdam keeps one second moment per row and no
- *        first moment.
+ *     pass 1 (logra_update_sqnorm): rowsq_i = sum_j Ghat_ij^2, the updated
+ *        row second moment v'_i = beta2 v_i + (1 - beta2) rowsq_i / k, and
+ *        the controller's reduction sqnorm = sum_ij (Ghat_ij / (sqrt(v'_i)+eps))^2;
+ *     pass 2 (logra_rowadam_apply): W_ij -= lr*scale*Ghat_ij / (sqrt(v'_i) + eps).
+ *   RowAdam keeps one second moment per row and no first moment. v' is a
+ *   separate buffer: the caller keeps it as the next step's v (swap the two
+ *   buffers) once it applies the update, and keeps v if it skips it. Pass 2
+ *   reads only (S, v', the step's key, lr*scale, eps), so the same call
+ *   rebuilds the update on any replica of W that receives those.
  *   A host-side step controller reads sqnorm between the two passes and
  *   picks scale. One is provided (logra_kl_step_scale, host code at the end
  *   of this header); a caller may use any other.
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LOGRA_ABI_VERSION 1
+#define LOGRA_ABI_VERSION 2
 
 typedef enum logra_status {
     LOGRA_OK = 0,
@@ -183,10 +186,10 @@ size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype);
 
 /*
  * logra_update_sqnorm -- apply pass 1. Rebuilds Ghat = S A tile by tile and
- * reduces, without changing any state:
- *   rowsq[i] = sum_j Ghat_ij^2                                  (d floats)
- *   sqnorm[0] = sum_i rowsq_i * u_i^2, u_i = 1/(sqrt(v'_i) + eps),
- *               v'_i = beta2 * v[i] + (1 - beta2) * rowsq_i / k
+ * reduces, without changing any input:
+ *   rowsq[i] = sum_j Ghat_ij^2                       (d floats, optional)
+ *   v_new[i] = beta2 * v[i] + (1 - beta2) * rowsq_i / k        (d floats)
+ *   sqnorm[0] = sum_i rowsq_i * u_i^2, u_i = 1/(sqrt(v_new_i) + eps)
  * sum_i rowsq_i u_i^2 equals sum_ij (Ghat_ij u_i)^2 because u is constant
  * along a row. sqnorm is the per-matrix quantity a predicted-KL step
  * controller reads before the update ("LoGRA: Scaling LLM Reinforcement
@@ -196,41 +199,50 @@ size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype);
  * Arguments:
  *   compute_dtype LOGRA_BF16: S is rounded to bf16 (nearest even) as the
  *            MFMA operand, fp32 accumulation. LOGRA_F32: fp32 arithmetic.
- *   S        d x r fp32 (stride r). v: d fp32 (current second moment).
- *   rowsq    d fp32, out. sqnorm: 1 fp32 on the device, out.
+ *   S        d x r fp32 (stride r). v: d fp32 (current second moment), in.
+ *   v_new    d fp32, out (must not alias v).
+ *   rowsq    d fp32, out, or NULL when not wanted.
+ *   sqnorm   1 fp32 on the device, out.
  *   ws       device workspace of ws_bytes >= logra_sqnorm_workspace_bytes().
  * Requirements: bf16 path r in {32, 64, 128, 256} and k multiple of 8; fp32
  *   path r in [1, 1024]. Pointers 16-byte aligned.
  * Errors: INVALID_ARGUMENT (nulls, sizes, beta2 outside [0,1], eps < 0,
- *   misalignment), UNSUPPORTED, WORKSPACE, HIP.
+ *   misalignment, v_new == v), UNSUPPORTED, WORKSPACE, HIP.
  */
 logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype,
                                  const float *S, const float *v,
                                  float beta2, float eps,
-                                 float *rowsq, float *sqnorm,
+                                 float *v_new, float *rowsq, float *sqnorm,
                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
- * logra_rowadam_apply -- apply pass 2. Commits v[i] <- v'_i and updates
- *   W_ij <- W_ij - lr * scale * Ghat_ij / (sqrt(v'_i) + eps)
- * with Ghat = S A rebuilt tile by tile and v'_i from the rowsq that
- * logra_update_sqnorm produced for the same S, v, beta2 (RowAdam, "NVIDIA's
- * LoGRA fits RL post-training...", sections "What happened" and "Why it
- * matters"; the update is rebuilt from the two small factors at the moment
- * it is applied, same page). scale is the step controller's factor.
+ * logra_rowadam_apply -- apply pass 2:
+ *   W_ij <- W_ij - lr * scale * Ghat_ij / (sqrt(v_new_i) + eps)
+ * with Ghat = S A rebuilt tile by tile and v_new the second moment that
+ * logra_update_sqnorm produced for the same S (RowAdam, "NVIDIA's LoGRA fits
+ * RL post-training...", sections "What happened" and "Why it matters"; the
+ * update is rebuilt from the two small factors at the moment it is applied,
+ * same page). scale is the step controller's factor. Nothing but W is
+ * written. Because the call needs only (S, v_new, the matrix's seed, step and
+ * id, lr*scale, eps), it is also how a copy of W elsewhere (a rollout
+ * worker's policy) is brought up to date from the sketch instead of from W
+ * itself: the low-rank representations serve policy synchronisation too
+ * ("LoGRA: Scaling LLM Reinforcement Learning...", abstract). Identical inputs
+ * give bit-identical W on every device of this architecture.
  * Arguments:
  *   compute_dtype as in logra_update_sqnorm.
- *   S        d x r fp32. v: d fp32, in/out. rowsq: d fp32, in.
+ *   S        d x r fp32. v_new: d fp32, in.
  *   W        d x k, row stride ldw >= k, dtype w_dtype (fp32 math, stored
  *            back at its dtype; bf16 by round-to-nearest-even), in/out.
  * Requirements: as logra_update_sqnorm; bf16 W or bf16 compute also need
  *   ldw multiple of 8 and W 16-byte aligned.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP, as above.
+ * Errors: INVALID_ARGUMENT (nulls, eps < 0, ld, misalignment), UNSUPPORTED,
+ *   HIP.
  */
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype,
-                                 const float *S, float *v, const float *rowsq,
+                                 const float *S, const float *v_new,
                                  void *W, int w_dtype, int64_t ldw,
-                                 float lr, float scale, float beta2, float eps,
+                                 float lr, float scale, float eps,
                                  void *stream);
 
 /*

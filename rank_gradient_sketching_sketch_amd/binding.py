@@ -83,9 +83,9 @@ def load_library():
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
-    lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, sz, P]
+    lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
-    lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, P, i32, i64, f32, f32, f32, f32, P]
+    lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, i32, i64, f32, f32, f32, P]
     dbl = ctypes.c_double
     lib.logra_kl_budget_at.restype = dbl
     lib.logra_kl_budget_at.argtypes = [ctypes.POINTER(KLBudget), u64]
@@ -184,23 +184,26 @@ def logra_sqnorm_workspace_bytes(m: MatrixDesc, compute_dtype: int) -> int:
 
 
 def logra_update_sqnorm(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
-                        beta2: float, eps: float, rowsq: torch.Tensor, sqnorm: torch.Tensor,
-                        ws: Optional[torch.Tensor] = None, stream=None) -> None:
+                        beta2: float, eps: float, v_new: torch.Tensor, sqnorm: torch.Tensor,
+                        rowsq: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """Pass 1: v_new <- beta2 v + (1 - beta2) rowsq / k, sqnorm, and rowsq if given."""
     if ws is None:
         nbytes = logra_sqnorm_workspace_bytes(m, compute_dtype)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=S.device)
     ws_bytes = ws.numel() * ws.element_size()
     _check(load_library().logra_update_sqnorm(
         ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
-        _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws_bytes, _stream(stream)), "logra_update_sqnorm")
+        _ptr(v_new), _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws_bytes, _stream(stream)),
+        "logra_update_sqnorm")
 
 
-def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
-                        rowsq: torch.Tensor, W: torch.Tensor, lr: float, scale: float,
-                        beta2: float, eps: float, stream=None) -> None:
+def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v_new: torch.Tensor,
+                        W: torch.Tensor, lr: float, scale: float, eps: float, stream=None) -> None:
+    """Pass 2: W -= lr * scale * (S A) / (sqrt(v_new) + eps), row-wise; writes W only."""
     _check(load_library().logra_rowadam_apply(
-        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), _ptr(rowsq), _ptr(W),
-        _dtype_code(W), _ld(W), float(lr), float(scale), float(beta2), float(eps),
+        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v_new), _ptr(W),
+        _dtype_code(W), _ld(W), float(lr), float(scale), float(eps),
         _stream(stream)), "logra_rowadam_apply")
 
 

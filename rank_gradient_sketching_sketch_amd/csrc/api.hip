@@ -204,16 +204,18 @@ static ApplyArgs base_args(const logra_matrix *m, const float *S, float beta2, f
 }
 
 logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const float *S,
-                                 const float *v, float beta2, float eps, float *rowsq,
-                                 float *sqnorm, void *ws, size_t ws_bytes, void *stream) {
+                                 const float *v, float beta2, float eps, float *v_new,
+                                 float *rowsq, float *sqnorm, void *ws, size_t ws_bytes,
+                                 void *stream) {
     logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
     if (stt != LOGRA_OK) return stt;
-    if (!v || !rowsq || !sqnorm) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!v || !v_new || !sqnorm || v_new == v) return LOGRA_ERR_INVALID_ARGUMENT;
     const size_t need = sqnorm_ws_bytes(m, compute_dtype);
     if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     ApplyArgs a = base_args(m, S, beta2, eps);
     a.v_in = v;
+    a.v_new_out = v_new;
     a.rowsq_out = rowsq;
     a.sqnorm = sqnorm;
     if (compute_dtype == LOGRA_BF16) return from_hip(launch_sqnorm_bf16(a, ws, st));
@@ -223,20 +225,19 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const
 }
 
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const float *S,
-                                 float *v, const float *rowsq, void *W, int w_dtype, int64_t ldw,
-                                 float lr, float scale, float beta2, float eps, void *stream) {
-    logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
+                                 const float *v_new, void *W, int w_dtype, int64_t ldw,
+                                 float lr, float scale, float eps, void *stream) {
+    logra_status stt = check_apply_common(m, compute_dtype, S, 0.f, eps);
     if (stt != LOGRA_OK) return stt;
-    if (!v || !rowsq || !W) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!v_new || !W) return LOGRA_ERR_INVALID_ARGUMENT;
     if (w_dtype != LOGRA_F32 && w_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
     if (ldw < m->k) return LOGRA_ERR_INVALID_ARGUMENT;
     if (compute_dtype == LOGRA_BF16 && (ldw % 8 || !aligned16(W))) return LOGRA_ERR_INVALID_ARGUMENT;
     if (compute_dtype == LOGRA_BF16 && !fits_view(m->d, ldw, w_dtype == LOGRA_BF16 ? 2 : 4))
         return LOGRA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    ApplyArgs a = base_args(m, S, beta2, eps);
-    a.v = v;
-    a.rowsq_in = rowsq;
+    ApplyArgs a = base_args(m, S, 0.f, eps);
+    a.v_new_in = v_new;
     a.lr_scale = lr * scale;
     a.W = W;
     a.w_bf16 = w_dtype == LOGRA_BF16 ? 1 : 0;

@@ -30,8 +30,9 @@
 // and are not written) and is requested one tile ahead of its products (two
 // ahead of its update, which lags the products by one unit).
 //
-// Every workgroup of a row tile reads v and rowsq to form u_i; v itself is
-// committed by a separate small pass once all of them are done.
+// u_i comes from the updated second moment v' that pass 1 wrote; nothing
+// but W is written, so the same kernel rebuilds the update on any replica
+// of W that receives S and v'.
 #include "common.hpp"
 #include "launch.hpp"
 #include "signs.hpp"
@@ -187,8 +188,7 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
             const int i = rt * kApplyRows + tid;
             float coef = 0.f;
             if (i < D) {
-                const float vn = a.beta2 * a.v[i] + (1.f - a.beta2) * (a.rowsq_in[i] / static_cast<float>(K));
-                coef = a.lr_scale * a.c / (sqrtf(vn) + a.eps);
+                coef = a.lr_scale * a.c / (sqrtf(a.v_new_in[i]) + a.eps);
             }
             coef_s[tid] = coef;
         }
@@ -340,19 +340,6 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
         finish(prev, cf_prev, pp, wb[1]);
 }
 
-// v <- beta2 v + (1 - beta2) rowsq / k, after every workgroup of the apply has read v.
-__global__ __launch_bounds__(256) void commit_v_kernel(float *__restrict__ v, const float *__restrict__ rowsq,
-                                                       int D, float beta2, float inv_k) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < D) v[i] = beta2 * v[i] + (1.f - beta2) * (rowsq[i] * inv_k);
-}
-
-hipError_t launch_commit_v(float *v, const float *rowsq, int64_t D, int64_t K, float beta2, hipStream_t st) {
-    hipLaunchKernelGGL(commit_v_kernel, dim3((D + 255) / 256), dim3(256), 0, st, v, rowsq,
-                       static_cast<int>(D), beta2, 1.f / static_cast<float>(K));
-    return hipGetLastError();
-}
-
 template <int R>
 static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
     const int n_rt = static_cast<int>((a.D + kApplyRows - 1) / kApplyRows);
@@ -365,9 +352,7 @@ static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
     else
         hipLaunchKernelGGL((rowadam_bf16_kernel<R, false>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
                            n_units);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_commit_v(a.v, a.rowsq_in, a.D, a.K, a.beta2, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st) {

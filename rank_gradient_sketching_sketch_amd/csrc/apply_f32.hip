@@ -1,6 +1,6 @@
 // fp32 twin of the apply passes: Ghat = S A rebuilt in fp32 (no
 // reduced-precision products), then pass 1 (rowsq, controller partials) or
-// pass 2 (RowAdam update). Same definitions as the bf16 kernels ("NVIDIA's
+// pass 2 (RowAdam update from v'). Same definitions as the bf16 kernels ("NVIDIA's
 // LoGRA fits RL post-training...", sections "What happened" and "Why it
 // matters"; "LoGRA: Scaling LLM Reinforcement Learning...", paragraph "Step
 // control."). A workgroup owns 8 rows; each of its 256 threads takes one
@@ -35,10 +35,8 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(ApplyArgs a) {
         const int ii = i0 + tid;
         float coef = 0.f;
         if (ii < D) {
-            const float vn = a.beta2 * a.v[ii] + (1.f - a.beta2) * (a.rowsq_in[ii] / static_cast<float>(K));
-            const float u = 1.f / (sqrtf(vn) + a.eps);
+            const float u = 1.f / (sqrtf(a.v_new_in[ii]) + a.eps);
             coef = a.lr_scale * a.c * u;
-            a.v[ii] = vn;
         }
         coef_s[tid] = coef;
     }
@@ -81,8 +79,9 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(ApplyArgs a) {
             float term = 0.f;
             if (i < D) {
                 const float rq = (a.c * a.c) * ss;
-                a.rowsq_out[i] = rq;
+                if (a.rowsq_out) a.rowsq_out[i] = rq;
                 const float vn = a.beta2 * a.v_in[i] + (1.f - a.beta2) * (rq / static_cast<float>(K));
+                a.v_new_out[i] = vn;
                 const float u = 1.f / (sqrtf(vn) + a.eps);
                 term = rq * u * u;
             }

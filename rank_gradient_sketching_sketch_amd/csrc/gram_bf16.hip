@@ -91,7 +91,8 @@ template <int R>
 __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict__ S, int D, int K,
                                                          const uint16_t *__restrict__ M, float c,
                                                          const float *__restrict__ v, float beta2,
-                                                         float eps, float *__restrict__ rowsq,
+                                                         float eps, float *__restrict__ v_new,
+                                                         float *__restrict__ rowsq,
                                                          float *__restrict__ partials, int bpw,
                                                          int *__restrict__ counter, float *__restrict__ sqnorm) {
     constexpr int KS = R / 32;                    // 32-wide steps of the rank
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
     }
     __syncthreads();
 
-    // 4. rowsq, v' and the controller's term, one thread per row
+    // 4. rowsq, v' (both stored) and the controller's term, one thread per row
     float term = 0.f;
     if (tid < rows) {
         const float2 p0 = part[0][tid], p1 = part[1][tid], p2 = part[2][tid], p3 = part[3][tid];
@@ -185,8 +186,9 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
         const float sq = ((p0.y + p1.y) + p2.y) + p3.y;
         const int i = r0 + tid;
         const float rq = (c * c) * fmaf(static_cast<float>(K), sq, yd);
-        rowsq[i] = rq;
+        if (rowsq) rowsq[i] = rq;
         const float vn = beta2 * v[i] + (1.f - beta2) * (rq / static_cast<float>(K));
+        v_new[i] = vn;
         const float u = 1.f / (sqrtf(vn) + eps);
         term = rq * u * u;
     }
@@ -245,7 +247,7 @@ static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, hipStream_t st) {
     const int K = static_cast<int>(a.K);
     hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter);
     hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
-                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.rowsq_out, partials,
+                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out, partials,
                        p.rows_per_block / 16, counter, a.sqnorm);
     return hipGetLastError();
 }

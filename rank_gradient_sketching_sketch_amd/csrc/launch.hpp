@@ -73,10 +73,10 @@ struct ApplyArgs {
     uint64_t key = 0;
     float c = 0.f;
     const float *S = nullptr;
-    const float *v_in = nullptr;   // mode 0
-    float *v = nullptr;            // mode 1 (in/out)
-    const float *rowsq_in = nullptr;
-    float *rowsq_out = nullptr;
+    const float *v_in = nullptr;       // pass 1: current second moment
+    float *v_new_out = nullptr;        // pass 1: updated second moment
+    float *rowsq_out = nullptr;        // pass 1: row sums of squares (may be null)
+    const float *v_new_in = nullptr;   // pass 2: updated second moment
     float *partials = nullptr;
     float *sqnorm = nullptr;
     float beta2 = 0.f, eps = 0.f, lr_scale = 0.f;
@@ -85,12 +85,10 @@ struct ApplyArgs {
     int64_t ldw = 0;
 };
 
-// bf16 compute: pass 1 (Gram form, writes rowsq and sqnorm) and pass 2
-// (RowAdam update of W, then v committed).
+// bf16 compute: pass 1 (Gram form, writes v', rowsq and sqnorm) and pass 2
+// (RowAdam update of W from S and v').
 hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st);
 hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st);
-hipError_t launch_commit_v(float *v, const float *rowsq, int64_t D, int64_t K, float beta2,
-                           hipStream_t st);
 // fp32 compute: mode 0 = pass 1 (rowsq + partials), mode 1 = pass 2 (W and v).
 hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);
 hipError_t launch_sqnorm_final(const float *partials, int n, float *out, hipStream_t st);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
-    assert B.logra_abi_version() == 1
+    assert B.logra_abi_version() == 2
     assert B.logra_status_string(0) == "LOGRA_OK"
     assert B.logra_status_string(3) == "LOGRA_ERR_WORKSPACE"
     assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
@@ -76,21 +76,26 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, None, 1 << 20, None) == 3
     # T == 0 with accumulate: nothing to do, no launch
     assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None) == 0
-    # apply passes: beta2 out of range, eps < 0, nulls, unsupported
-    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(1.5), ctypes.c_float(1e-8),
-                                   FAKE, FAKE, FAKE, 1 << 20, None) == 1
-    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(-1.0),
-                                   FAKE, FAKE, FAKE, 1 << 20, None) == 1
-    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
-                                   FAKE, None, FAKE, 1 << 20, None) == 1
-    assert lib.logra_update_sqnorm(r(m), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
-                                   FAKE, FAKE, FAKE, 0, None) == 3
-    assert lib.logra_update_sqnorm(r(m48), 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
-                                   FAKE, FAKE, FAKE, 1 << 20, None) == 2
-    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, FAKE, 1, 100, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(0.9), ctypes.c_float(1e-8), None) == 1
-    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, FAKE, 5, 128, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(0.9), ctypes.c_float(1e-8), None) == 2
+    # apply passes: beta2 out of range, eps < 0, nulls, v' aliasing v, unsupported
+    V2 = ctypes.c_void_p(0x20000)
+    def sq(beta2, eps, v_new=V2, sqn=FAKE, ws_bytes=1 << 20, mm=m):
+        return lib.logra_update_sqnorm(r(mm), 1, FAKE, FAKE, ctypes.c_float(beta2), ctypes.c_float(eps),
+                                       v_new, None, sqn, FAKE, ws_bytes, None)
+    assert sq(1.5, 1e-8) == 1
+    assert sq(0.9, -1.0) == 1
+    assert sq(0.9, 1e-8, sqn=None) == 1
+    assert sq(0.9, 1e-8, v_new=None) == 1
+    assert sq(0.9, 1e-8, v_new=FAKE) == 1          # v' must not alias v
+    assert sq(0.9, 1e-8, ws_bytes=0) == 3
+    assert sq(0.9, 1e-8, mm=m48) == 2
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 100, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 1
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, None, FAKE, 1, 128, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 1
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 128, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(-1.0), None) == 1
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 5, 128, ctypes.c_float(1e-3),
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 2
     assert lib.logra_sign_words(None, FAKE, None) == 1
 
 

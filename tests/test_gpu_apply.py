@@ -29,14 +29,17 @@ def _state(seed, d, k, r, s_std=1e-2):
 
 def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev):
     S_d, v_d, W_d = S.to(dev), v.clone().to(dev), W.clone().to(dev)
+    v_new = torch.empty(m.d, dtype=torch.float32, device=dev)
     rowsq = torch.empty(m.d, dtype=torch.float32, device=dev)
     sq = torch.empty(1, dtype=torch.float32, device=dev)
-    B.logra_update_sqnorm(m, compute, S_d, v_d, beta2, eps, rowsq, sq)
+    B.logra_update_sqnorm(m, compute, S_d, v_d, beta2, eps, v_new, sq, rowsq)
     torch.cuda.synchronize()
     rowsq_h, sq_h = rowsq.cpu(), sq.item()
-    B.logra_rowadam_apply(m, compute, S_d, v_d, rowsq, W_d, lr, scale, beta2, eps)
+    B.logra_rowadam_apply(m, compute, S_d, v_new, W_d, lr, scale, eps)
     torch.cuda.synchronize()
-    return rowsq_h, sq_h, v_d.cpu(), W_d.cpu()
+    # pass 1 leaves v as it was
+    assert torch.equal(v_d.cpu(), v)
+    return rowsq_h, sq_h, v_new.cpu(), W_d.cpu()
 
 
 APPLY_CASES = [
@@ -151,3 +154,42 @@ def test_apply_deterministic_and_nan_propagates():
     S[7, 3] = float("nan")
     rowsq, sq, _, _ = _run(m, B.LOGRA_BF16, S, v, W, 1e-3, 1.0, 0.99, 1e-8, dev)
     assert np.isnan(sq) and torch.isnan(rowsq[7]) and not torch.isnan(rowsq[8])
+
+
+@pytest.mark.parametrize("wdt", [torch.bfloat16, torch.float32])
+def test_policy_sync_replica_matches_trainer(wdt):
+    # A rollout worker's copy of W is brought up to date from the sketch alone:
+    # it receives (S, v', the matrix's seed/step/id, lr * scale, eps) instead of
+    # W or a dense update, and pass 2 rebuilds the same update there. The
+    # replica must equal the trainer's W bit for bit, and both must match the
+    # oracle's RowAdam step (beta2 = 1 on v' reproduces the update from v').
+    dev = device()
+    d, k, r = 1032, 4104, 256
+    m = B.MatrixDesc(d, k, r, seed=13, step=4, matrix_id=6)
+    S, v, W = _state(17, d, k, r)
+    W = W.to(wdt)
+    lr, scale, beta2, eps = 1e-3, 0.6, 0.999, 1e-8
+    S_d, v_d = S.to(dev), v.to(dev)
+    v_new = torch.empty(d, dtype=torch.float32, device=dev)
+    sq = torch.empty(1, dtype=torch.float32, device=dev)
+    B.logra_update_sqnorm(m, B.LOGRA_BF16, S_d, v_d, beta2, eps, v_new, sq)
+    W_trainer, W_replica = W.clone().to(dev), W.clone().to(dev)
+    B.logra_rowadam_apply(m, B.LOGRA_BF16, S_d, v_new, W_trainer, lr, scale, eps)
+    # the message: S and v' (copied, as a transfer would), plus scalars
+    msg_S, msg_v = S_d.clone(), v_new.clone()
+    B.logra_rowadam_apply(B.MatrixDesc(d, k, r, seed=13, step=4, matrix_id=6), B.LOGRA_BF16,
+                          msg_S, msg_v, W_replica, lr, scale, eps)
+    torch.cuda.synchronize()
+    assert torch.equal(W_trainer.cpu(), W_replica.cpu())
+    msg_bytes = (msg_S.numel() + msg_v.numel()) * 4
+    say("  policy sync: %d bytes instead of %d (W)" % (msg_bytes, W.numel() * W.element_size()))
+    assert msg_bytes * 3 < W.numel() * W.element_size()
+    A = oracle.sign_matrix(13, 4, 6, r, k)
+    ref = oracle.rowadam_rows(S.double().numpy(), A, to_f64(v_new), W.double().numpy(),
+                              beta2=1.0, eps=f32(eps), lr=f32(lr), scale=f32(scale))
+    W0 = W.double().numpy()
+    if wdt == torch.float32:
+        assert w_update_err(to_f64(W_replica), ref["W_new"], W0) < BF16_TOL
+    else:
+        ok, _ = bf16_w_check(to_f64(W_replica), ref["W_new"], W0)
+        assert ok

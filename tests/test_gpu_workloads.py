@@ -60,24 +60,25 @@ def _step_and_check(wl, spec, step, st, dev, mbs, T, tol, data_seed=0):
     compute = _code(wl.act_dtype)
     W, v, W32 = st["W"], st["v"], st["W32"]
     rowsq = torch.empty(d, dtype=torch.float32, device=dev)
+    v_new = torch.empty(d, dtype=torch.float32, device=dev)
     sq = torch.empty(1, dtype=torch.float32, device=dev)
-    v_gpu_old = v.clone()
-    B.logra_update_sqnorm(m, compute, S, v, beta2, eps, rowsq, sq)
+    B.logra_update_sqnorm(m, compute, S, v, beta2, eps, v_new, sq, rowsq)
     torch.cuda.synchronize()
     # sqnorm identity over all rows, from the GPU's own rowsq and v (a property
     # of the GPU outputs; no oracle input)
-    rowsq_h, v_old_h = to_f64(rowsq), to_f64(v_gpu_old)
+    rowsq_h, v_old_h = to_f64(rowsq), to_f64(v)
     vn = hp["beta2"] * v_old_h + (1 - hp["beta2"]) * rowsq_h / k
     ident = float((rowsq_h / (np.sqrt(vn) + hp["eps"]) ** 2).sum())
     e_ident = abs(sq.item() / ident - 1)
 
     ref = oracle.rowadam_rows(S_ref, A, st["v_ref"], st["W_ref"], **hp)
     e_rq = rel_err(rowsq_h[rows], ref["rowsq"])
-    B.logra_rowadam_apply(m, compute, S, v, rowsq, W, lr, scale, beta2, eps)
+    B.logra_rowadam_apply(m, compute, S, v_new, W, lr, scale, eps)
     if W32 is not None:
-        B.logra_rowadam_apply(m, compute, S, v_gpu_old, rowsq, W32, lr, scale, beta2, eps)
+        B.logra_rowadam_apply(m, compute, S, v_new, W32, lr, scale, eps)
     torch.cuda.synchronize()
-    e_v = rel_err(to_f64(v)[rows], ref["v_new"])
+    e_v = rel_err(to_f64(v_new)[rows], ref["v_new"])
+    st["v"] = v_new   # the update was applied: v' is the next step's v
     W_new = to_f64(W)[rows]
     if W.dtype == torch.bfloat16:
         w_ok, _ = bf16_w_check(W_new, ref["W_new"], st["W_ref"], steps=step + 1)
