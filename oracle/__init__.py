@@ -4,9 +4,11 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only permitted callers. The product path (the HIP
 library and its binding) never imports this package.
 
-The arithmetic lives in ``oracle.c`` (plain fp64 C, built with gcc). This
-module only marshals numpy arrays into it; every array passed in is converted
-to a C-contiguous float64 (or int64/uint64) copy first.
+The arithmetic of the sketch and the RowAdam step lives in ``oracle.c``
+(plain fp64 C, built with gcc). This module only marshals numpy arrays into
+it; every array passed in is converted to a C-contiguous float64 (or
+int64/uint64) copy first. The host step controller's oracle is plain Python
+in ``oracle/controller.py``.
 """
 from __future__ import annotations
 

@@ -193,3 +193,22 @@ def test_policy_sync_replica_matches_trainer(wdt):
     else:
         ok, _ = bf16_w_check(to_f64(W_replica), ref["W_new"], W0)
         assert ok
+
+
+@pytest.mark.parametrize("compute", [B.LOGRA_BF16, B.LOGRA_F32])
+def test_rowsq_output_is_optional(compute):
+    # rowsq == NULL: the same v' and sqnorm, bit for bit, as with rowsq requested
+    dev = device()
+    d, k, r = 1032, 1544, 256 if compute == B.LOGRA_BF16 else 48
+    m = B.MatrixDesc(d, k, r, 6, 2, 9)
+    S, v, _ = _state(23, d, k, r)
+    S_d, v_d = S.to(dev), v.to(dev)
+    outs = []
+    for want_rowsq in (True, False):
+        v_new = torch.empty(d, device=dev)
+        sq = torch.empty(1, device=dev)
+        rowsq = torch.empty(d, device=dev) if want_rowsq else None
+        B.logra_update_sqnorm(m, compute, S_d, v_d, 0.999, 1e-8, v_new, sq, rowsq)
+        torch.cuda.synchronize()
+        outs.append((v_new.cpu(), sq.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
