@@ -2,9 +2,11 @@
 
 One step = every microbatch of the step folded into the sketch
 (logra_sketch_project + logra_sketch_fold, i.e. logra_sketch_accumulate),
-pass 1 (logra_update_sqnorm) for every matrix, one device-to-host read of the
-sqnorms for the step controller, and pass 2 (logra_rowadam_apply) for every
-matrix. Inputs are synthetic and already resident in HBM; each microbatch of
+pass 1 (logra_update_sqnorm, v -> v') for every matrix, one device-to-host
+read of the sqnorms for the step controller (the library's host controller
+runs on them and its decision is reported; the update uses the workload's
+drawn scale), pass 2 (logra_rowadam_apply) for every matrix, and the swap of
+v and v'. Inputs are synthetic and already resident in HBM; each microbatch of
 a step has its own buffers, so the inputs of one step (about 3 GB in the
 default workload) stream through the 256 MB last-level cache.
 
