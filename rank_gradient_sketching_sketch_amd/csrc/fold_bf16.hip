@@ -294,16 +294,19 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         bload(s_begin + p, pb[p]);
     }
 
-    u32x4_t a_cur[MBW], a_nxt[MBW];
+    // dY^T fragments, double-buffered by step parity (PF is even, so the
+    // buffer of a step is a compile-time index and nothing is copied)
+    static_assert(PF % 2 == 0, "an even prefetch depth keeps the fragment buffers fixed");
+    u32x4_t afr[2][MBW];
 #pragma unroll
-    for (int j = 0; j < MBW; ++j) a_cur[j] = a_nxt[j] = zero_u32x4();
+    for (int j = 0; j < MBW; ++j) afr[0][j] = afr[1][j] = zero_u32x4();
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         lstore(s_begin, raw[0][k], k);
         raw[0][k] = gload(s_begin + PF, k);
     }
     lds_barrier();
-    aread(s_begin, a_cur);
+    aread(s_begin, afr[0]);
 
     // Whole groups of PF steps; up to PF-1 steps past s_end load zeros and
     // add nothing.
@@ -319,18 +322,16 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
                 raw[(p + 1) % PF][k] = gload(s + 1 + PF, k);
             }
             lds_barrier();
-            aread(s + 1, a_nxt);
+            aread(s + 1, afr[(p + 1) % 2]);
 #pragma unroll
             for (int j = 0; j < MBW; ++j) {
                 if (j < MBW - 1 || wm + j * WM < nmb) {
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
-                        acc[j][nb] = mfma_bf16(a_cur[j], pb[p][nb], acc[j][nb]);
+                        acc[j][nb] = mfma_bf16(afr[p % 2][j], pb[p][nb], acc[j][nb]);
                 }
             }
             bload(s + PF, pb[p]);
-#pragma unroll
-            for (int j = 0; j < MBW; ++j) a_cur[j] = a_nxt[j];
         }
     }
 
