@@ -6,17 +6,19 @@
 // "Why it matters"); RowAdam keeps one running second moment per row and no
 // first moment (same page, "What happened" and "Why it matters").
 //
-// Work decomposition. The unit of work is one 256-row tile of W times one
-// 64-column tile; the units, in row-major order, are dealt to a fixed number
-// of workgroups as contiguous ranges of equal cost, counting the load of a
-// row tile's S rows as a few units (one workgroup per compute unit), so a
-// workgroup touches at most a few row tiles and loads their rows of S only
-// once each. Neighbouring ranges (which share a row
-// tile) run on the same XCD, so S is fetched from HBM about once and the
-// other workgroups of the row tile find it in that XCD's L2. Eight waves
+// Work decomposition. The unit of work is one row tile of W (256 rows, or
+// 128 when the matrix is too small to give every workgroup at least four
+// 256-row units) times one 64-column tile; the units, in row-major order,
+// are dealt to a fixed number of workgroups as contiguous ranges of equal
+// cost, counting the load of a row tile's S rows as a few units (one
+// workgroup per compute unit), so a workgroup touches at most a few row tiles
+// and loads their rows of S only once each. Neighbouring ranges (which share
+// a row tile) run on the same XCD, so S is fetched from HBM about once and
+// the other workgroups of the row tile find it in that XCD's L2. Eight waves
 // (two per SIMD, so one wave's vector work overlaps the other's matrix work)
-// each own 32 of the 256 rows and keep S^T for them as bf16 MFMA operands in
-// registers.
+// each own 32 (or 16) of the tile's rows and keep S^T for them as bf16 MFMA
+// operands in registers. The 128-row tiles halve the S a workgroup loads for
+// its few units (1536 x 1536: 13.5 instead of 18.9 us per call).
 //
 // Per column tile: every thread hashes one 64-bit sign word (rank row l,
 // these 64 columns) into LDS; each wave then builds an eighth of the tile's
@@ -40,10 +42,11 @@
 namespace logra {
 
 constexpr uint32_t kOobOff = 0x80000000u;
-constexpr int kApplyRows = 256;        // rows of W per row tile (32 per wave)
+constexpr int kApplyRowsMax = 256;     // rows of W per row tile, most (32 per wave)
 constexpr int kApplyWaves = 8;
 constexpr int kApplyCols = 64;         // columns per column tile (one sign word)
 constexpr int kApplyWGs = 256;         // workgroups (one per compute unit)
+constexpr int kTallTileUnitsPerWG = 4;  // 256-row units per workgroup from which 256-row tiles are used
 constexpr int kStagePitch = 144;       // bytes per staged row of a wave's updated bf16 block
 
 // Barrier that orders LDS traffic only (global loads stay in flight).
@@ -53,8 +56,10 @@ __device__ __forceinline__ void apply_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int R, bool WBF16>
+template <int R, bool WBF16, int RB>
 __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct, int n_units) {
+    constexpr int kApplyRows = 128 * RB;       // rows of W per row tile (16 RB per wave)
+    constexpr int WR = 16 * RB;                // rows per wave
     constexpr int KS = R / 32;                 // 32-wide steps of the rank
     constexpr int WV = WBF16 ? 1 : 2;          // 16-byte vectors per 8 columns of W
     constexpr int NF = 4 * KS;                 // sign fragments per column tile
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // bf16 W: each wave's updated 32 x 64 block on its way from the MFMA
     // layout to whole-line stores (rows padded to 144 bytes: conflict-free
     // both ways)
-    __shared__ __attribute__((aligned(16))) uint8_t wstage[WBF16 ? kApplyWaves * 32 * kStagePitch : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t wstage[WBF16 ? kApplyWaves * WR * kStagePitch : 16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -109,14 +114,14 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // Byte offset of lane (n, g)'s 8 columns of row block rb, column half h,
     // in unit p (kOobOff if masked).
     auto w_off = [&](const Pos &p, int rb, int h) -> uint32_t {
-        const int i = p.rt * kApplyRows + 32 * wave + 16 * rb + n;
+        const int i = p.rt * kApplyRows + WR * wave + 16 * rb + n;
         const int jc = p.ct * kApplyCols + 32 * h + 8 * g;
         const bool ok = p.u < u_end && i < D && jc < K;
         return ok ? static_cast<uint32_t>((static_cast<int64_t>(i) * a.ldw + jc) * (WBF16 ? 2 : 4)) : kOobOff;
     };
-    auto w_load = [&](const Pos &p, u32x4_t (&w)[2][2][WV]) {
+    auto w_load = [&](const Pos &p, u32x4_t (&w)[RB][2][WV]) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t off = w_off(p, rb, h);
@@ -168,12 +173,12 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     // S^T fragments of the current row tile: lane (n, g) of row block rb,
     // step s holds S[i][32 s + 8 g .. +7] in bf16, i = row 32 wave + 16 rb + n
     // of the tile (rows past d are clamped: their products are never stored).
-    u32x4_t sf[2][KS];
+    u32x4_t sf[RB][KS];
     int cur_rt = -1;
     auto load_rows = [&](int rt) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int i = min(rt * kApplyRows + 32 * wave + 16 * rb + n, D - 1);
+        for (int rb = 0; rb < RB; ++rb) {
+            const int i = min(rt * kApplyRows + WR * wave + 16 * rb + n, D - 1);
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const float *p = a.S + static_cast<int64_t>(i) * R + 32 * s + 8 * g;
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
 
     // W_ij -= cf_i * (Ghat/c)_ij for the unit at p: lane (n, g) of (rb, cb)
     // holds row 32 wave + 16 rb + n, columns 32 (cb / 2) + 8 g + 4 (cb % 2) .. +3.
-    auto finish = [&](const f32x4_t (&acc)[2][4], const float (&cf)[2], const Pos &p,
-                      const u32x4_t (&wv)[2][2][WV]) {
+    auto finish = [&](const f32x4_t (&acc)[RB][4], const float (&cf)[RB], const Pos &p,
+                      const u32x4_t (&wv)[RB][2][WV]) {
         if (WBF16) {
             // The MFMA layout gives each lane 16 bytes of one row, so a wave's
             // store would cover 16 rows x 64 bytes (half cache lines). The
@@ -206,9 +211,9 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
             // rows x 128 bytes per instruction (lane L: row 8 q + L / 8,
             // columns 8 (L % 8) .. +7), whole lines, which HBM takes much
             // faster.
-            uint8_t *blk = wstage + wave * 32 * kStagePitch;
+            uint8_t *blk = wstage + wave * WR * kStagePitch;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
@@ -226,10 +231,10 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
             const int lr = lane >> 3, lc = lane & 7;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2 * RB; ++q) {
                 const int row = 8 * q + lr;
                 const u32x4_t o = *reinterpret_cast<const u32x4_t *>(blk + row * kStagePitch + 16 * lc);
-                const int i = p.rt * kApplyRows + 32 * wave + row;
+                const int i = p.rt * kApplyRows + WR * wave + row;
                 const int jc = p.ct * kApplyCols + 8 * lc;
                 const uint32_t off = (p.u < u_end && i < D && jc < K)
                                          ? static_cast<uint32_t>((static_cast<int64_t>(i) * a.ldw + jc) * 2)
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         } else {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const f32x4_t x0 = acc[rb][2 * h], x1 = acc[rb][2 * h + 1];
@@ -270,16 +275,18 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
     pp.u = u_end;   // none yet: w_off masks every access of a unit >= u_end
     Pos p1 = advance(p0);   // the unit whose W is requested
     Pos p2 = advance(p1);   // the unit whose sign words are requested
-    u32x4_t wb[2][2][2][WV];   // W ring: slot (u - u_begin) % 2 holds unit u
+    u32x4_t wb[2][RB][2][WV];   // W ring: slot (u - u_begin) % 2 holds unit u
     w_load(p0, wb[0]);
     hash_words(p0, 0);
     apply_lds_barrier();
     build_frags(0);
     hash_words(p1, 1);
-    f32x4_t prev[2][4];
-    float cf_prev[2] = {0.f, 0.f};
+    f32x4_t prev[RB][4];
+    float cf_prev[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb) cf_prev[rb] = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) prev[rb][cb] = zero_f32x4();
 
@@ -300,9 +307,9 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
                     load_rows(p0.rt);
                 }
                 apply_lds_barrier();   // fragments of u and words of u + 1 are in LDS
-                f32x4_t acc[2][4];
+                f32x4_t acc[RB][4];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = zero_f32x4();
 #pragma unroll
@@ -311,17 +318,17 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
                     for (int cb = 0; cb < 4; ++cb) {
                         const u32x4_t af = frags[buf][cb * KS + s][lane];
 #pragma unroll
-                        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = mfma_bf16(af, sf[rb][s], acc[rb][cb]);
+                        for (int rb = 0; rb < RB; ++rb) acc[rb][cb] = mfma_bf16(af, sf[rb][s], acc[rb][cb]);
                     }
-                float cf_cur[2];
+                float cf_cur[RB];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) cf_cur[rb] = coef_s[32 * wave + 16 * rb + n];
+                for (int rb = 0; rb < RB; ++rb) cf_cur[rb] = coef_s[WR * wave + 16 * rb + n];
                 finish(prev, cf_prev, pp, wb[(p + 1) % 2]);   // unit u - 1 (slot (u - 1) % 2)
                 w_load(p1, wb[(p + 1) % 2]);                 // unit u + 1 into the freed slot
                 build_frags(buf ^ 1);
                 hash_words(p2, buf);
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < RB; ++rb) {
                     cf_prev[rb] = cf_cur[rb];
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb) prev[rb][cb] = acc[rb][cb];
@@ -340,19 +347,30 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
         finish(prev, cf_prev, pp, wb[1]);
 }
 
-template <int R>
-static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
-    const int n_rt = static_cast<int>((a.D + kApplyRows - 1) / kApplyRows);
+template <int R, int RB>
+static hipError_t rowadam_rb(const ApplyArgs &a, hipStream_t st) {
+    constexpr int rows = 128 * RB;
+    const int n_rt = static_cast<int>((a.D + rows - 1) / rows);
     const int n_ct = static_cast<int>((a.K + kApplyCols - 1) / kApplyCols);
     const int n_units = n_rt * n_ct;
     const int grid = n_units < kApplyWGs ? n_units : kApplyWGs;
     if (a.w_bf16)
-        hipLaunchKernelGGL((rowadam_bf16_kernel<R, true>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
+        hipLaunchKernelGGL((rowadam_bf16_kernel<R, true, RB>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
                            n_units);
     else
-        hipLaunchKernelGGL((rowadam_bf16_kernel<R, false>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
+        hipLaunchKernelGGL((rowadam_bf16_kernel<R, false, RB>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
                            n_units);
     return hipGetLastError();
+}
+
+// Row tiles of 256 rows when each workgroup gets enough units of them to
+// amortise loading its rows of S (256 KB at r = 256), otherwise 128 rows,
+// which halve that load at the price of sign fragments shared by fewer rows.
+template <int R>
+static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
+    const int64_t units256 = ((a.D + kApplyRowsMax - 1) / kApplyRowsMax) * ((a.K + kApplyCols - 1) / kApplyCols);
+    if (units256 >= static_cast<int64_t>(kTallTileUnitsPerWG) * kApplyWGs) return rowadam_rb<R, 2>(a, st);
+    return rowadam_rb<R, 1>(a, st);
 }
 
 hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st) {
