@@ -212,3 +212,39 @@ def test_rowsq_output_is_optional(compute):
         torch.cuda.synchronize()
         outs.append((v_new.cpu(), sq.cpu()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_controller_scale_through_the_gpu_update_meets_the_budget():
+    # f1 end to end on the hot path: sqnorms from pass 1 on the GPU, the
+    # library's host controller picks gamma for a budget a quarter of the
+    # predicted KL, pass 2 applies lr * gamma; the realised 1/2 phi ||dW||^2
+    # of the GPU's fp32 W update (over three matrices) must equal the budget
+    # within the bf16-compute tolerance, and gamma = 1/2 exactly.
+    dev = device()
+    lr, phi, beta2, eps = 2e-3, 0.5, 0.999, 1e-8
+    shapes = [(520, 1544, 256), (1032, 4104, 256), (200, 520, 64)]
+    mats, sqs = [], []
+    for idx, (d, k, r) in enumerate(shapes):
+        m = B.MatrixDesc(d, k, r, 7, 11, idx)
+        S, v, W = _state(31 + idx, d, k, r)
+        S_d, v_d = S.to(dev), v.to(dev)
+        v_new = torch.empty(d, device=dev)
+        sq = torch.empty(1, device=dev)
+        B.logra_update_sqnorm(m, B.LOGRA_BF16, S_d, v_d, beta2, eps, v_new, sq)
+        mats.append((m, S_d, v_new, W.to(dev)))
+        sqs.append(sq)
+    torch.cuda.synchronize()
+    sq_h = [float(q.item()) for q in sqs]
+    _, kl0, _ = B.logra_kl_step_scale(sq_h, lr, phi, 1e30)
+    delta = 0.25 * kl0
+    scales, kl_pred, kl_after = B.logra_kl_step_scale(sq_h, lr, phi, delta)
+    assert np.allclose(scales, 0.5, rtol=1e-6) and abs(kl_after / delta - 1) < 1e-9
+    dw2 = 0.0
+    for (m, S_d, v_new, W_d), sc in zip(mats, scales):
+        W0 = W_d.clone()
+        B.logra_rowadam_apply(m, B.LOGRA_BF16, S_d, v_new, W_d, lr, float(sc), eps)
+        torch.cuda.synchronize()
+        dw2 += float(((W_d.double() - W0.double()) ** 2).sum().item())
+    realised = 0.5 * phi * dw2
+    say("  controller: predicted %.4e, budget %.4e, realised after scaling %.4e" % (kl_pred, delta, realised))
+    assert abs(realised / delta - 1) < BF16_TOL
