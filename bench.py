@@ -58,6 +58,8 @@ def parse():
                     help="streams the matrices' sketch calls are spread over (0: at most 4)")
     ap.add_argument("--apply-streams", type=int, default=0,
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="pass 1 one matrix per call instead of batches of up to 16 per stream")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -151,6 +153,27 @@ def main():
     for i, m in enumerate(mats):
         m["lane"] = lanes[i % n_sketch]
         m["alane"] = lanes[i % n_apply]
+    # Pass 1 in batches: each apply stream's matrices in chunks of up to
+    # B.MAX_BATCH, one call (two launches) per chunk; a chunk of one matrix
+    # uses the single-matrix call. Each batched matrix's sqnorm is a view of
+    # its chunk's n-float output.
+    batches = []
+    batch_ws_bytes = 0
+    if not args.no_batch:
+        for ln in lanes[:n_apply]:
+            own = [m for m in mats if m["alane"] is ln]
+            for c0 in range(0, len(own), B.MAX_BATCH):
+                chunk = own[c0:c0 + B.MAX_BATCH]
+                if len(chunk) == 1:
+                    batches.append((ln, chunk, None, None))
+                    continue
+                sq = torch.empty(len(chunk), dtype=torch.float32, device=dev)
+                for i, m in enumerate(chunk):
+                    m["sq"] = sq[i:i + 1]
+                wsb = B.logra_sqnorm_batch_workspace_bytes(
+                    [B.MatrixDesc(m["spec"].d, m["spec"].k, r) for m in chunk], code)
+                batch_ws_bytes += wsb
+                batches.append((ln, chunk, sq, torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)))
     # Microbatch buffers: every microbatch has its own; layer stacks rotate
     # two sets of per-layer inputs (even and odd layers), which keeps a
     # 28- or 64-layer step within memory while consecutive layers still read
@@ -229,10 +252,21 @@ def main():
         join()
         e1 = ev() if timed else None
         fork()
-        for m in mats:
-            ln = m["alane"]
-            B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
-                                  m["sq"], None, ln["sq_ws"], ln["stream"])
+        if batches:
+            for ln, chunk, sq, bws in batches:
+                if sq is None:
+                    m = chunk[0]
+                    B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
+                                          m["sq"], None, ln["sq_ws"], ln["stream"])
+                else:
+                    B.logra_update_sqnorm_batch([m["desc"] for m in chunk], code, [m["S"] for m in chunk],
+                                                [m["v"] for m in chunk], wl.beta2, wl.eps,
+                                                [m["v_new"] for m in chunk], sq, None, bws, ln["stream"])
+        else:
+            for m in mats:
+                ln = m["alane"]
+                B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
+                                      m["sq"], None, ln["sq_ws"], ln["stream"])
         join()
         e2 = ev() if timed else None
         # one device->host read of every sqnorm; the library's host controller
@@ -339,8 +373,9 @@ def main():
                    "weights": sum(m["W"].numel() * m["W"].element_size() for m in mats),
                    "microbatch_inputs": sum(t.numel() * t.element_size()
                                             for t in list(xbuf.values()) + list(ybuf.values())),
-                   "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes))},
-        "streams": {"sketch": n_sketch, "apply": n_apply},
+                   "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes)) + batch_ws_bytes},
+        "streams": {"sketch": n_sketch, "apply": n_apply,
+                    "pass1_batches": sum(1 for b in batches if b[2] is not None)},
         "controller": {"fisher_scale": KL_PHI,
                        "budget": [kl_budget.delta_start, kl_budget.delta_end, kl_budget.anneal_steps],
                        "kl_pred_last_step": ctl_log[-1][1], "gamma_last_step": ctl_log[-1][2],

@@ -216,6 +216,33 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype,
                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * logra_update_sqnorm_batch -- pass 1 of n matrices in one call (1 <= n <=
+ * LOGRA_MAX_BATCH), exactly what n calls of logra_update_sqnorm would give
+ * (same arithmetic, bit-identical outputs), with two kernel launches in all
+ * on the bf16 path instead of two per matrix. For the many small
+ * projections of a layer (attention's k and v fill a fraction of the chip
+ * each) the launches, not the bytes, set the time. Sources: as
+ * logra_update_sqnorm.
+ * Arguments (host arrays of n entries; the pointers in them are device
+ * pointers with the meaning they have in logra_update_sqnorm):
+ *   ms       the matrices; all with the same r.
+ *   S, v, v_new  per matrix; rowsq NULL (none wanted) or an array whose
+ *            entries may be NULL.
+ *   sqnorm   n fp32 on the device, out (entry i for matrix i).
+ *   ws       device workspace of ws_bytes >= logra_sqnorm_batch_workspace_bytes().
+ * Errors: as logra_update_sqnorm for any matrix, and INVALID_ARGUMENT for n
+ *   outside [1, LOGRA_MAX_BATCH], NULL arrays or differing r. Nothing is
+ *   launched on error.
+ */
+#define LOGRA_MAX_BATCH 16
+size_t logra_sqnorm_batch_workspace_bytes(int n, const logra_matrix *ms, int compute_dtype);
+logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int compute_dtype,
+                                       const float *const *S, const float *const *v,
+                                       float beta2, float eps,
+                                       float *const *v_new, float *const *rowsq, float *sqnorm,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+/*
  * logra_rowadam_apply -- apply pass 2:
  *   W_ij <- W_ij - lr * scale * Ghat_ij / (sqrt(v_new_i) + eps)
  * with Ghat = S A rebuilt tile by tile and v_new the second moment that

@@ -86,6 +86,11 @@ def load_library():
     lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
     lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, i32, i64, f32, f32, f32, P]
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.logra_sqnorm_batch_workspace_bytes.restype = sz
+    lib.logra_sqnorm_batch_workspace_bytes.argtypes = [i32, D, i32]
+    lib.logra_update_sqnorm_batch.restype = i32
+    lib.logra_update_sqnorm_batch.argtypes = [i32, D, i32, PP, PP, f32, f32, PP, PP, P, P, sz, P]
     dbl = ctypes.c_double
     lib.logra_kl_budget_at.restype = dbl
     lib.logra_kl_budget_at.argtypes = [ctypes.POINTER(KLBudget), u64]
@@ -224,3 +229,41 @@ def logra_kl_step_scale(sqnorm, lr: float, fisher_scale: float, delta: float):
         out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(kl_pred), ctypes.byref(kl_after)),
         "logra_kl_step_scale")
     return out, kl_pred.value, kl_after.value
+
+
+MAX_BATCH = 16
+
+
+def _matrix_array(ms):
+    arr = (MatrixDesc * len(ms))()
+    for i, m in enumerate(ms):
+        arr[i] = m
+    return arr
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in ts])
+
+
+def logra_sqnorm_batch_workspace_bytes(ms, compute_dtype: int) -> int:
+    return int(load_library().logra_sqnorm_batch_workspace_bytes(len(ms), _matrix_array(ms),
+                                                                  int(compute_dtype)))
+
+
+def logra_update_sqnorm_batch(ms, compute_dtype: int, S, v, beta2: float, eps: float, v_new,
+                              sqnorm: torch.Tensor, rowsq=None, ws: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """Pass 1 of several matrices of one rank in one call (lists of tensors;
+    sqnorm: device tensor of len(ms) floats)."""
+    n = len(ms)
+    if ws is None:
+        nbytes = logra_sqnorm_batch_workspace_bytes(ms, compute_dtype)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=sqnorm.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    rq = None if rowsq is None else ctypes.cast(_ptr_array(rowsq), ctypes.POINTER(ctypes.c_void_p))
+    _check(load_library().logra_update_sqnorm_batch(
+        n, _matrix_array(ms), int(compute_dtype),
+        ctypes.cast(_ptr_array(S), ctypes.POINTER(ctypes.c_void_p)),
+        ctypes.cast(_ptr_array(v), ctypes.POINTER(ctypes.c_void_p)), float(beta2), float(eps),
+        ctypes.cast(_ptr_array(v_new), ctypes.POINTER(ctypes.c_void_p)), rq, _ptr(sqnorm), _ptr(ws),
+        ws_bytes, _stream(stream)), "logra_update_sqnorm_batch")

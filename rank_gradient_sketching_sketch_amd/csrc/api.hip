@@ -224,6 +224,85 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const
     return from_hip(launch_sqnorm_final(a.partials, apply_blocks_f32(m->d), sqnorm, st));
 }
 
+// Workspace slice of matrix i of a batch: the single-matrix layout, each
+// slice 256-byte aligned.
+static size_t batch_slice_bytes(const logra_matrix *m, int compute_dtype) {
+    return (sqnorm_ws_bytes(m, compute_dtype) + 255) / 256 * 256;
+}
+
+size_t logra_sqnorm_batch_workspace_bytes(int n, const logra_matrix *ms, int compute_dtype) {
+    if (n < 1 || n > LOGRA_MAX_BATCH || !ms) return 0;
+    if (compute_dtype != LOGRA_F32 && compute_dtype != LOGRA_BF16) return 0;
+    size_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        if (!matrix_ok(&ms[i])) return 0;
+        total += batch_slice_bytes(&ms[i], compute_dtype);
+    }
+    return total;
+}
+
+logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int compute_dtype,
+                                       const float *const *S, const float *const *v, float beta2,
+                                       float eps, float *const *v_new, float *const *rowsq,
+                                       float *sqnorm, void *ws, size_t ws_bytes, void *stream) {
+    if (n < 1 || n > LOGRA_MAX_BATCH || !ms || !S || !v || !v_new || !sqnorm)
+        return LOGRA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < n; ++i) {
+        const logra_status e = check_apply_common(&ms[i], compute_dtype, S[i], beta2, eps);
+        if (e != LOGRA_OK) return e;
+        if (ms[i].r != ms[0].r) return LOGRA_ERR_INVALID_ARGUMENT;
+        if (!v[i] || !v_new[i] || v_new[i] == v[i]) return LOGRA_ERR_INVALID_ARGUMENT;
+    }
+    if (!aligned16(sqnorm)) return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = logra_sqnorm_batch_workspace_bytes(n, ms, compute_dtype);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    if (compute_dtype == LOGRA_F32) {
+        // the fp32 twin: the single-matrix passes one after another
+        for (int i = 0; i < n; ++i) {
+            ApplyArgs a = base_args(&ms[i], S[i], beta2, eps);
+            a.v_in = v[i];
+            a.v_new_out = v_new[i];
+            a.rowsq_out = rowsq ? rowsq[i] : nullptr;
+            a.sqnorm = sqnorm + i;
+            a.partials = reinterpret_cast<float *>(base);
+            if (launch_apply_f32(0, a, st) != hipSuccess) return LOGRA_ERR_HIP;
+            if (launch_sqnorm_final(a.partials, apply_blocks_f32(ms[i].d), a.sqnorm, st) != hipSuccess)
+                return LOGRA_ERR_HIP;
+            base += batch_slice_bytes(&ms[i], compute_dtype);
+        }
+        return LOGRA_OK;
+    }
+    SqnormBatch b;
+    b.n = n;
+    b.beta2 = beta2;
+    b.eps = eps;
+    b.sqnorm = sqnorm;
+    int wg = 0;
+    for (int i = 0; i < n; ++i) {
+        const SqnormPlan p = plan_sqnorm_bf16(ms[i].d, ms[i].k, static_cast<int>(ms[i].r));
+        SqnormItem &it = b.item[i];
+        it.S = S[i];
+        it.v = v[i];
+        it.v_new = v_new[i];
+        it.rowsq = rowsq ? rowsq[i] : nullptr;
+        it.partials = reinterpret_cast<float *>(base);
+        it.M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
+        it.counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
+        it.key = stream_key(ms[i].seed, ms[i].step, ms[i].matrix_id);
+        it.c = inv_sqrt_rank(ms[i].r);
+        it.D = static_cast<int>(ms[i].d);
+        it.K = static_cast<int>(ms[i].k);
+        it.bpw = p.rows_per_block / 16;
+        it.wg_begin = wg;
+        it.n_wg = p.n_blocks;
+        wg += p.n_blocks;
+        base += batch_slice_bytes(&ms[i], compute_dtype);
+    }
+    return from_hip(launch_sqnorm_batch_bf16(static_cast<int>(ms[0].r), b, st));
+}
+
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const float *S,
                                  const float *v_new, void *W, int w_dtype, int64_t ldw,
                                  float lr, float scale, float eps, void *stream) {

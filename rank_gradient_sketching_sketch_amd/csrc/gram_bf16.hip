@@ -31,14 +31,14 @@ namespace logra {
 // differences of its pair.
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
-__global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
-                                                   int *__restrict__ counter) {
+__device__ __forceinline__ void gram_body(uint64_t key, int R, int K, uint16_t *__restrict__ M,
+                                          int *__restrict__ counter, int bx, int by) {
     __shared__ uint64_t wl[16][kGramChunk + 1];
     __shared__ uint64_t wm[16][kGramChunk + 1];
     const int tid = threadIdx.x;
     // the rowsq kernel that follows counts its workgroups from zero
-    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *counter = 0;
-    const int l0 = blockIdx.y * 16, m0 = blockIdx.x * 16;
+    if (bx == 0 && by == 0 && tid == 0) *counter = 0;
+    const int l0 = by * 16, m0 = bx * 16;
     const int tl = tid >> 4, tm = tid & 15;
     const int nb = (K + 63) / 64;
     const int tail = K - 64 * (nb - 1);
@@ -68,6 +68,11 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
     M[(static_cast<size_t>(frag) * 64 + ln) * 8 + (m & 7)] = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+__global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
+                                                   int *__restrict__ counter) {
+    gram_body(key, R, K, M, counter, blockIdx.x, blockIdx.y);
+}
+
 // rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
 // owns bpw blocks of 16 rows of S (the plan makes about one workgroup per
 // compute unit) and stages them in LDS as fp32 (rows padded by 16 bytes, so
@@ -88,13 +93,12 @@ constexpr int kRowsqMaxBlocks = 8;   // 16-row blocks of S per workgroup (most)
 constexpr int kRowsqWGs = 256;       // target workgroups (one per compute unit)
 
 template <int R>
-__global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict__ S, int D, int K,
-                                                         const uint16_t *__restrict__ M, float c,
-                                                         const float *__restrict__ v, float beta2,
-                                                         float eps, float *__restrict__ v_new,
-                                                         float *__restrict__ rowsq,
-                                                         float *__restrict__ partials, int bpw,
-                                                         int *__restrict__ counter, float *__restrict__ sqnorm) {
+__device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, int K,
+                                           const uint16_t *__restrict__ M, float c,
+                                           const float *__restrict__ v, float beta2, float eps,
+                                           float *__restrict__ v_new, float *__restrict__ rowsq,
+                                           float *__restrict__ partials, int bpw, int *__restrict__ counter,
+                                           float *__restrict__ sqnorm, int blk, int nblk) {
     constexpr int KS = R / 32;                    // 32-wide steps of the rank
     constexpr int NB = R / 16;                    // 16-row blocks of m
     constexpr int MPW = NB >= 4 ? NB / 4 : 1;     // blocks of m per wave
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int r0 = blockIdx.x * bpw * 16;
+    const int r0 = blk * bpw * 16;
     const int rows = min(bpw * 16, D - r0);
     const int mb0 = wave * MPW;
     const bool active = mb0 < NB;                 // r = 32: two of the four waves have no m block
@@ -199,17 +203,17 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
     __syncthreads();
     if (tid == 0) {
         const float pw = ((terms[0] + terms[1]) + terms[2]) + terms[3];
-        __hip_atomic_store(partials + blockIdx.x, pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(partials + blk, pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is stored before the count
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == static_cast<int>(gridDim.x) - 1;
+        last = prev == nblk - 1;
         if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!last) return;
     // sqnorm = the partials added in a fixed order: strided per thread, then a tree
     float t = 0.f;
-    for (int i = tid; i < static_cast<int>(gridDim.x); i += 256)
+    for (int i = tid; i < nblk; i += 256)
         t += __hip_atomic_load(partials + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     red[tid] = t;
     __syncthreads();
@@ -218,6 +222,39 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
         __syncthreads();
     }
     if (tid == 0) sqnorm[0] = red[0];
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict__ S, int D, int K,
+                                                         const uint16_t *__restrict__ M, float c,
+                                                         const float *__restrict__ v, float beta2,
+                                                         float eps, float *__restrict__ v_new,
+                                                         float *__restrict__ rowsq,
+                                                         float *__restrict__ partials, int bpw,
+                                                         int *__restrict__ counter, float *__restrict__ sqnorm) {
+    rowsq_body<R>(S, D, K, M, c, v, beta2, eps, v_new, rowsq, partials, bpw, counter, sqnorm, blockIdx.x,
+                  gridDim.x);
+}
+
+// Pass 1 of several matrices of one rank in two launches: the Gram matrices
+// of all of them (grid z = matrix), then every matrix's row blocks in one
+// grid, each workgroup finding its matrix from the running block counts.
+// Each matrix keeps its own workspace slice, counter and sqnorm, and the
+// per-matrix arithmetic is the single-matrix kernels' own, so the results
+// are bit-identical to calling them one matrix at a time.
+template <int R>
+__global__ __launch_bounds__(256) void gram_batch_kernel(SqnormBatch b) {
+    const SqnormItem &it = b.item[blockIdx.z];
+    gram_body(it.key, R, it.K, it.M, it.counter, blockIdx.x, blockIdx.y);
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void rowsq_batch_kernel(SqnormBatch b) {
+    int j = 0;
+    while (j + 1 < b.n && static_cast<int>(blockIdx.x) >= b.item[j + 1].wg_begin) ++j;
+    const SqnormItem &it = b.item[j];
+    rowsq_body<R>(it.S, it.D, it.K, it.M, it.c, it.v, b.beta2, b.eps, it.v_new, it.rowsq, it.partials, it.bpw,
+                  it.counter, b.sqnorm + j, static_cast<int>(blockIdx.x) - it.wg_begin, it.n_wg);
 }
 
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
@@ -250,6 +287,25 @@ static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, hipStream_t st) {
                        static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out, partials,
                        p.rows_per_block / 16, counter, a.sqnorm);
     return hipGetLastError();
+}
+
+template <int R>
+static hipError_t sqnorm_batch_r(const SqnormBatch &b, hipStream_t st) {
+    int total = 0;
+    for (int j = 0; j < b.n; ++j) total += b.item[j].n_wg;
+    hipLaunchKernelGGL(gram_batch_kernel<R>, dim3(R / 16, R / 16, b.n), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(rowsq_batch_kernel<R>, dim3(total), dim3(256), 0, st, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_sqnorm_batch_bf16(int R, const SqnormBatch &b, hipStream_t st) {
+    switch (R) {
+    case 32: return sqnorm_batch_r<32>(b, st);
+    case 64: return sqnorm_batch_r<64>(b, st);
+    case 128: return sqnorm_batch_r<128>(b, st);
+    case 256: return sqnorm_batch_r<256>(b, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st) {

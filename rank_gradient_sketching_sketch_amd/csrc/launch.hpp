@@ -85,6 +85,31 @@ struct ApplyArgs {
     int64_t ldw = 0;
 };
 
+// Pass 1 of up to kSqnormBatchMax matrices of one rank (bf16 compute), each
+// with its own slice of the workspace laid out as SqnormPlan says.
+constexpr int kSqnormBatchMax = 16;
+struct SqnormItem {
+    const float *S = nullptr;
+    const float *v = nullptr;
+    float *v_new = nullptr;
+    float *rowsq = nullptr;        // may be null
+    uint16_t *M = nullptr;         // Gram matrix in the item's workspace slice
+    float *partials = nullptr;
+    int *counter = nullptr;
+    uint64_t key = 0;
+    float c = 0.f;
+    int D = 0, K = 0;
+    int bpw = 0;                   // 16-row blocks per workgroup
+    int wg_begin = 0, n_wg = 0;    // the item's workgroups in the batch grid
+};
+struct SqnormBatch {
+    int n = 0;
+    float beta2 = 0.f, eps = 0.f;
+    float *sqnorm = nullptr;       // n floats
+    SqnormItem item[kSqnormBatchMax];
+};
+hipError_t launch_sqnorm_batch_bf16(int R, const SqnormBatch &b, hipStream_t st);
+
 // bf16 compute: pass 1 (Gram form, writes v', rowsq and sqnorm) and pass 2
 // (RowAdam update of W from S and v').
 hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st);

@@ -130,3 +130,26 @@ def test_state_size_is_d_by_r():
     state = 4 * d * r + 4 * d
     dense = 4 * d * k
     assert abs(dense / (4 * d * r) - k / r) < 1e-12 and state < dense / 13
+
+
+def test_sqnorm_batch_validation_and_workspace(lib):
+    from rank_gradient_sketching_sketch_amd import binding as B
+    ms = [B.MatrixDesc(18944, 3584, 256), B.MatrixDesc(512, 3584, 256), B.MatrixDesc(3584, 18944, 256)]
+    single = [B.logra_sqnorm_workspace_bytes(m, B.LOGRA_BF16) for m in ms]
+    # the single-matrix layouts one after another, each slice 256-byte aligned
+    assert B.logra_sqnorm_batch_workspace_bytes(ms, B.LOGRA_BF16) == sum((b + 255) // 256 * 256 for b in single)
+    arr = B._matrix_array(ms)
+    ptrs = (ctypes.c_void_p * 3)(0x10000, 0x20000, 0x30000)
+    vptr = (ctypes.c_void_p * 3)(0x40000, 0x50000, 0x60000)
+    vnew = (ctypes.c_void_p * 3)(0x70000, 0x80000, 0x90000)
+    PP = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))
+    call = lambda n, m, vn=vnew, ws=FAKE, wsb=1 << 30: lib.logra_update_sqnorm_batch(
+        n, m, 1, PP(ptrs), PP(vptr), ctypes.c_float(0.9), ctypes.c_float(1e-8), PP(vn), None, FAKE, ws, wsb, None)
+    assert call(0, arr) == 1                      # n < 1
+    assert call(17, arr) == 1                     # n > LOGRA_MAX_BATCH
+    assert call(3, arr, vn=vptr) == 1             # v' aliasing v
+    assert call(3, arr, wsb=16) == 3              # workspace too small
+    assert call(3, arr, ws=None) == 3
+    mixed = B._matrix_array([ms[0], B.MatrixDesc(512, 3584, 128), ms[2]])
+    assert call(3, mixed) == 1                    # ranks differ
+    assert B.logra_sqnorm_batch_workspace_bytes([], B.LOGRA_BF16) == 0

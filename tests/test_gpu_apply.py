@@ -248,3 +248,34 @@ def test_controller_scale_through_the_gpu_update_meets_the_budget():
     realised = 0.5 * phi * dw2
     say("  controller: predicted %.4e, budget %.4e, realised after scaling %.4e" % (kl_pred, delta, realised))
     assert abs(realised / delta - 1) < BF16_TOL
+
+
+@pytest.mark.parametrize("compute", [B.LOGRA_BF16, B.LOGRA_F32])
+def test_sqnorm_batch_equals_single_calls(compute):
+    # pass 1 of several matrices in one call == one call per matrix, bit for
+    # bit (v', rowsq where requested, sqnorm), shapes from one to many
+    # workgroups per matrix and a ragged last workgroup
+    dev = device()
+    r = 256 if compute == B.LOGRA_BF16 else 40
+    shapes = [(520, 1544), (256, 1536), (8200, 136), (1032, 4104), (40, 72)]
+    ms, S, v = [], [], []
+    for i, (d, k) in enumerate(shapes):
+        ms.append(B.MatrixDesc(d, k, r, 3, 5, 20 + i))
+        Si, vi, _ = _state(50 + i, d, k, r)
+        S.append(Si.to(dev))
+        v.append(vi.to(dev))
+    v_new_b = [torch.full((m.d,), -1.0, device=dev) for m in ms]
+    rowsq_b = [torch.full((m.d,), -1.0, device=dev) if i % 2 == 0 else None for i, m in enumerate(ms)]
+    sq_b = torch.full((len(ms),), -1.0, device=dev)
+    B.logra_update_sqnorm_batch(ms, compute, S, v, 0.999, 1e-8, v_new_b, sq_b, rowsq_b)
+    torch.cuda.synchronize()
+    for i, m in enumerate(ms):
+        v_new = torch.empty(m.d, device=dev)
+        rowsq = torch.empty(m.d, device=dev)
+        sq = torch.empty(1, device=dev)
+        B.logra_update_sqnorm(m, compute, S[i], v[i], 0.999, 1e-8, v_new, sq, rowsq)
+        torch.cuda.synchronize()
+        assert torch.equal(v_new, v_new_b[i]), i
+        assert torch.equal(sq[0], sq_b[i]), i
+        if rowsq_b[i] is not None:
+            assert torch.equal(rowsq, rowsq_b[i]), i
