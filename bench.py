@@ -60,6 +60,9 @@ def parse():
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="also time torch.mm (the vendor GEMM) on the fold's contraction and on the "
+                         "dense dY^T X it replaces, for context")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -383,9 +386,55 @@ def main():
                        "applied": False},
     }
 
+    if args.yardstick:
+        result["yardstick"] = yardstick(wl, fold_ms if len(mats) == 1 else None)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
+
+
+def yardstick(wl, fold_ms):
+    """Context only, not the product path: the vendor GEMM behind torch.mm on
+    the largest matrix's shapes, (a) the fold's contraction dY^T P (d x T x r)
+    and (b) the dense gradient dY^T X (d x T x k) that the sketch never forms.
+    Operands are contiguous bf16 (dY^T materialised once), rotated over three
+    sets so that no launch finds its inputs in the last-level cache."""
+    import torch
+    spec = max(wl.matrices, key=lambda s: s.d * s.k)
+    d, k, T, r = spec.d, spec.k, wl.tokens, wl.r
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(1)
+    sets = [((torch.randn(d, T, device="cuda:0", generator=g) * 1e-4).bfloat16(),
+             torch.randn(T, r, device="cuda:0", generator=g).bfloat16(),
+             torch.randn(T, k, device="cuda:0", generator=g).bfloat16()) for _ in range(3)]
+
+    def timed(fn, reps=21):
+        for i in range(3):
+            fn(i % 3)
+        torch.cuda.synchronize()
+        times = []
+        for i in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(i % 3)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return sorted(times)[reps // 2]
+
+    t_fold = timed(lambda i: torch.mm(sets[i][0], sets[i][1]))
+    t_dense = timed(lambda i: torch.mm(sets[i][0], sets[i][2]))
+    out = {"library": "torch.mm (bf16 in, bf16 out)", "shape_dTrk": [d, T, r, k],
+           "fold_contraction": {"us": round(t_fold * 1e3, 2),
+                                "tflops": round(2.0 * d * T * r / (t_fold * 1e-3) / 1e12, 1)},
+           "dense_gradient": {"us": round(t_dense * 1e3, 2),
+                              "tflops": round(2.0 * d * T * k / (t_dense * 1e-3) / 1e12, 1)}}
+    if fold_ms is not None:
+        out["logra_fold_us"] = round(fold_ms * 1e3, 2)
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, budget_s=15.0):
