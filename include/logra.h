@@ -177,6 +177,22 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
                                void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * logra_set_fold_wait_limit -- how long a fold workgroup waits for its
+ * partner. On the bf16 path, tall tiles are split over two token halves
+ * whose workgroups exchange partial sums inside the kernel; each polls the
+ * other's flag at most `polls` times (default 1 << 20, about a second) and,
+ * if the partner has not arrived, writes its rows of S as NaN instead of
+ * waiting longer. A negative value makes them give up without polling,
+ * which forces that path from the host (for tests of it). The setting is
+ * process-wide and applies to folds launched after the call; it is not
+ * synchronised with launches made at the same time from other threads.
+ * previous: host, may be NULL; receives the limit in force before the call.
+ * Not an operation of the pages: a guard of this implementation's exchange.
+ * Errors: none.
+ */
+logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous);
+
+/*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs
  * (per-block partial sums of the sqnorm reduction; on the bf16 path also the
  * r x r Gram matrix of the signs and a counter that the call zeroes itself).

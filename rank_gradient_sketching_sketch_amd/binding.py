@@ -80,6 +80,8 @@ def load_library():
     lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, P]
     lib.logra_sketch_fold.restype = i32
     lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, P]
+    lib.logra_set_fold_wait_limit.restype = i32
+    lib.logra_set_fold_wait_limit.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
@@ -165,6 +167,16 @@ def _sketch_ws(m, T, code, device, ws):
         nbytes = logra_sketch_workspace_bytes(m, T, code)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
+
+
+def logra_set_fold_wait_limit(polls: int) -> int:
+    """Polls a fold member makes for its partner before writing its rows as
+    NaN (negative: give up at once, to force that path); returns the previous
+    limit. Process-wide."""
+    prev = ctypes.c_int32(0)
+    _check(load_library().logra_set_fold_wait_limit(int(polls), ctypes.byref(prev)),
+           "logra_set_fold_wait_limit")
+    return int(prev.value)
 
 
 def logra_sketch_project(m: MatrixDesc, X: torch.Tensor, ws: torch.Tensor, stream=None) -> None:

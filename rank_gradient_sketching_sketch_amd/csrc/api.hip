@@ -58,6 +58,12 @@ const char *logra_status_string(int status) {
     }
 }
 
+logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous) {
+    const int prev = logra::set_fold_spin_limit(polls);
+    if (previous) *previous = prev;
+    return LOGRA_OK;
+}
+
 logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stream) {
     if (!matrix_ok(m) || !words) return LOGRA_ERR_INVALID_ARGUMENT;
     if (m->r > (1ll << 20)) return LOGRA_ERR_UNSUPPORTED;

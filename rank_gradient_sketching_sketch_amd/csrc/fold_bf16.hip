@@ -61,7 +61,18 @@ constexpr int kFoldSlots = 3;         // LDS ring slots (one step of 32 tokens e
 constexpr int kFoldMaxSplit = 32;     // members per tile (most)
 constexpr int kXcds = 8;              // gfx950: workgroup ids go round-robin over 8 XCDs
 constexpr int kFoldWGs = 256;         // one workgroup per compute unit
-constexpr int kFoldSpinLimit = 1 << 20;   // polls of a member's flag before giving up
+constexpr int kFoldSpinLimit = 1 << 20;   // polls of a member's flag before giving up (default)
+
+// The poll limit the launches pass (process-wide; logra_set_fold_wait_limit).
+// A negative limit makes a member of a pair give up without polling, which
+// forces the time-out path from the host.
+static int g_fold_spin_limit = kFoldSpinLimit;
+
+int set_fold_spin_limit(int polls) {
+    const int prev = g_fold_spin_limit;
+    g_fold_spin_limit = polls;
+    return prev;
+}
 
 // Shape of one kernel instance. MAXB (5 or 10) bounds the 16-row blocks of a
 // tile; tiles are planned to hold MAXB or MAXB - 1 blocks where d allows,
@@ -119,7 +130,7 @@ template <int R, int MAXB, int MODE>
 __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
     int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
-    int accumulate, int nblk, int n_tiles, int n_split, int steps_per) {
+    int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit) {
     using Sh = FoldShape<R, MAXB>;
     constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = Sh::PF, NCH = Sh::NCH;
     constexpr int kLdsRow = Sh::LDS_ROW;
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         if (tid == 0) {
             const int mine = static_cast<int>(__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u) + 1;
             int other = 0;
-            for (int spins = 0; spins <= kFoldSpinLimit; ++spins) {
+            for (int spins = 0; spins <= spin_limit; ++spins) {
                 other = __hip_atomic_load(xcd_of + ti * n_split + (1 - mem), __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
                 if (other != 0) break;
@@ -460,10 +471,14 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
                 int ok = 1;
                 for (int q = 0; q < n_split && ok; ++q) {
                     if (q == mem) continue;
+                    if (spin_limit < 0) {
+                        ok = 0;
+                        break;
+                    }
                     int spins = 0;
                     while (__hip_atomic_load(flags + ti * n_split + q, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                        if (++spins > kFoldSpinLimit) {
+                        if (++spins > spin_limit) {
                             ok = 0;
                             break;
                         }
@@ -634,7 +649,7 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
         kernel = fold_bf16_kernel<R, 10, kFoldSingle>;
     hipLaunchKernelGGL(kernel, dim3(p.n_tiles * p.n_split), dim3(256), 0, st, dY, lddy, static_cast<int>(T),
                        static_cast<int>(D), P, p_blocks, S, xbuf, static_cast<int>(p.xbuf_bytes), sync, accumulate,
-                       p.nblk, p.n_tiles, p.n_split, p.steps_per);
+                       p.nblk, p.n_tiles, p.n_split, p.steps_per, g_fold_spin_limit);
     if (p.n_split > 2) {
         const int64_t n = D * R;
         hipLaunchKernelGGL(fold_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, xbuf, p.n_split, n, S,

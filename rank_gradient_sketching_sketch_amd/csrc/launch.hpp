@@ -34,6 +34,9 @@ struct FoldPlan {
     size_t sync_bytes = 0;
 };
 FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
+// Sets the polls a fold member makes for its partner before it gives up and
+// writes its rows as NaN; returns the previous limit. Negative: give up at once.
+int set_fold_spin_limit(int polls);
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, hipStream_t st);

@@ -46,6 +46,18 @@ def test_abi_version_and_status_strings(lib):
     assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
 
 
+def test_fold_wait_limit_round_trip(lib):
+    # host-side setting only: returns the previous limit, default 1 << 20
+    from rank_gradient_sketching_sketch_amd import binding as B
+    prev = B.logra_set_fold_wait_limit(5)
+    try:
+        assert prev == 1 << 20
+        assert B.logra_set_fold_wait_limit(-1) == 5
+        assert lib.logra_set_fold_wait_limit(7, None) == 0   # previous may be NULL
+    finally:
+        assert B.logra_set_fold_wait_limit(prev) == 7
+
+
 def _m(d=64, k=128, r=32):
     from rank_gradient_sketching_sketch_amd import binding as B
     return B.MatrixDesc(d, k, r, 0, 0, 0)

@@ -130,6 +130,36 @@ def test_fold_twice_from_one_projection():
     assert torch.equal(S_acc, S1)
 
 
+def test_fold_wait_timeout_writes_nan_and_recovers():
+    # Forced from the host: with a negative wait limit the two members of
+    # every tile give up on each other at once and write their rows as NaN
+    # (every kernel still runs to its end). With the default limit back, a
+    # second fold from the same projection and workspace gives the exact
+    # result: the timed-out fold left its sync words usable.
+    dev = device()
+    T, d, k, r = 320, 8208, 96, 256   # d >= 8192: tiles over two token halves
+    say("fold wait time-out", T, d, k, r)
+    m = B.MatrixDesc(d, k, r, 1, 2, 3)
+    X, dY = inputs.random_case(78, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    X, dY = X.to(dev), dY.to(dev)
+    ws = torch.empty(B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+    S_ref = torch.empty(d, r, device=dev)
+    B.logra_sketch_accumulate(m, X, dY, S_ref, accumulate=False)
+    S = torch.zeros(d, r, device=dev)
+    B.logra_sketch_project(m, X, ws)
+    prev = B.logra_set_fold_wait_limit(-1)
+    try:
+        B.logra_sketch_fold(m, dY, S, False, ws)
+        torch.cuda.synchronize()
+    finally:
+        assert B.logra_set_fold_wait_limit(prev) == -1
+    assert prev == 1 << 20
+    assert torch.isnan(S).all()
+    B.logra_sketch_fold(m, dY, S, False, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref)
+
+
 F32_CASES = [
     (128, 256, 512, 32, 4),     # the tiny fp32 workload's shape
     (77, 45, 130, 20, 2),
