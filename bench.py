@@ -39,7 +39,7 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # + WRITE_SIZE x 1, the factors a plain device copy gives), per workload; see
 # profiles/hbm_traffic_qwen7b_up.md. Only valid for the fold kernel as it was
 # when the counters were taken.
-FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102533 * 2 + 37940) * 1024}
+FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102539 * 2 + 37940) * 1024}
 # Predicted-KL controller run on every step's sqnorms and reported: an
 # isotropic Fisher of scale 1 and a budget annealed from 1e-3 to 1e-4 nats
 # over 1000 steps (the pages give no values). The update itself uses the
