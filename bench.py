@@ -47,6 +47,31 @@ FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102539 * 2 + 37940) * 1024}
 KL_PHI = 1.0
 
 
+def sketch_flop_per_step(wl):
+    """Algorithmic FLOPs of one step's sketch: both products, 2 T r (d + k)
+    per matrix and microbatch (work the method avoids is not counted)."""
+    return sum(2.0 * wl.tokens * wl.r * (s.d + s.k) for s in wl.matrices) * wl.microbatches
+
+
+def fold_bytes_per_step(wl):
+    """Algorithmic bytes of one step's folds: dY and P read, S written, and S
+    also read when the fold accumulates (every microbatch but the first)."""
+    T, r = wl.tokens, wl.r
+    total = 0.0
+    for s in wl.matrices:
+        for mb in range(wl.microbatches):
+            total += 2.0 * T * s.d + 2.0 * T * r + 4.0 * s.d * r * (2 if mb > 0 else 1)
+    return total
+
+
+def apply_bytes_per_step(wl):
+    """Algorithmic bytes of one step's apply: W read and written at its
+    dtype, S read once, v read, v' written (pass 1) and read (pass 2)."""
+    import torch
+    wbytes = 2 if wl.w_dtype == torch.bfloat16 else 4
+    return sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * wl.r + 12.0 * s.d for s in wl.matrices)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,15 +235,9 @@ def main():
             e.record(ln["stream"])
             main.wait_event(e)
 
-    sketch_flop_per_step = sum(2.0 * T * r * (s.d + s.k) for s in wl.matrices) * nmb
-    fold_bytes_per_step = 0.0
-    for s in wl.matrices:
-        for mb in range(nmb):
-            fold_bytes_per_step += 2.0 * T * s.d + 2.0 * T * r + 4.0 * s.d * r * (2 if mb > 0 else 1)
-    wbytes = 2 if wl.w_dtype == torch.bfloat16 else 4
-    # W read and written, S read once, v read, v' written (pass 1) and read (pass 2)
-    apply_bytes_per_step = sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * r + 12.0 * s.d
-                               for s in wl.matrices)
+    sketch_flop = sketch_flop_per_step(wl)
+    fold_bytes = fold_bytes_per_step(wl)
+    apply_bytes = apply_bytes_per_step(wl)
 
     # Event records cost a few microseconds of GPU time each, so the timed
     # steps record events only at phase boundaries (sketch | pass 1 | pass 2).
@@ -333,9 +352,9 @@ def main():
     K = args.steps
     sketch_ms = tot["sketch"] / K
     apply_ms = (tot["sqnorm"] + tot["apply"]) / K
-    sketch_tflops = sketch_flop_per_step / (sketch_ms * 1e-3) / 1e12
-    apply_gbps = apply_bytes_per_step / (apply_ms * 1e-3) / 1e9
-    fold_bytes_avg = fold_bytes_per_step / (nmb * len(mats))
+    sketch_tflops = sketch_flop / (sketch_ms * 1e-3) / 1e12
+    apply_gbps = apply_bytes / (apply_ms * 1e-3) / 1e9
+    fold_bytes_avg = fold_bytes / (nmb * len(mats))
     dev_free, dev_total = torch.cuda.mem_get_info(dev)
     fold_gbps = fold_bytes_avg / (fold_ms * 1e-3) / 1e9
 
