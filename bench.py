@@ -298,13 +298,17 @@ def main():
         c0 = time.perf_counter()
         gamma, kl_pred, _ = B.logra_kl_step_scale(sqs, wl.lr, KL_PHI, B.logra_kl_budget_at(kl_budget, step))
         ctl_log.append((time.perf_counter() - c0, kl_pred, float(gamma.max()) if len(gamma) else 1.0))
-        e3 = ev() if timed else None
-        fork()
+        # the workload's drawn scales (input generation, kept out of the
+        # timed pass 2); a matrix with a non-finite sqnorm is skipped
+        todo = []
         for m, sq in zip(mats, sqs):
             if not math.isfinite(sq):
                 skipped[0] += 1
                 continue
-            scale = inputs.step_scale(wl, m["spec"], step)
+            todo.append((m, inputs.step_scale(wl, m["spec"], step)))
+        e3 = ev() if timed else None
+        fork()
+        for m, scale in todo:
             B.logra_rowadam_apply(m["desc"], code, m["S"], m["v_new"], m["W"], wl.lr, scale, wl.eps,
                                   m["alane"]["stream"])
             # the update is applied: v' becomes the next step's v (buffer swap)

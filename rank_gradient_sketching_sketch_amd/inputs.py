@@ -2,7 +2,7 @@
 
 This module holds no arithmetic of the method: it only draws the tensors the
 method consumes (activations X, output gradients dY, weights W, second
-moments v, the controller's scale) with the shapes and distributions of the
+moments v, the per-step scale) with the shapes and distributions of the
 Qwen-shaped workloads, so that the HIP path, the oracle and the benchmark all
 see the same data. Random numbers come from torch generators seeded by a hash
 of a descriptive key, so a tensor depends only on its key and size, never on
@@ -166,8 +166,9 @@ def second_moment(wl: Workload, spec: MatrixSpec, data_seed: int = 0, device="cp
 
 
 def step_scale(wl: Workload, spec: MatrixSpec, step: int, data_seed: int = 0) -> float:
-    """The controller's scale for one matrix and step (drawn, since the
-    controller itself is not part of this path)."""
+    """The step scale applied to one matrix in one step, drawn U(0.5, 1)
+    per the workload recipe (the predicted-KL controller's factor is
+    computed and reported alongside, not applied)."""
     if wl.scale_mode == "one":
         return 1.0
     g = generator("scale", wl.name, spec.matrix_id, step, data_seed)
