@@ -40,7 +40,9 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller (except the
  *     host arrays of the step controller at the end). The library
- *     allocates nothing, keeps no mutable global state and is reentrant.
+ *     allocates nothing and is reentrant; its one piece of mutable global
+ *     state is the fold's partner-wait limit (logra_set_fold_wait_limit),
+ *     a process-wide setting read when a fold is launched.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; results are visible after the caller
  *     synchronises the stream.
