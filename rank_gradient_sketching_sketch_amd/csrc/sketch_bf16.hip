@@ -29,12 +29,13 @@
 
 namespace logra {
 
-constexpr int kS1Tokens = 32;     // tokens per workgroup (two 16-row MFMA blocks)
+constexpr int kS1Tokens = 32;     // tokens per P block (the fold's operand layout)
 constexpr int kS1Waves = 8;       // waves per workgroup; they split the k range
 constexpr int kS1Words = 8;       // sign-word blocks (64 columns of k each) hashed per refill
 constexpr int kS1Prefetch = 2;    // steps of X held in registers ahead of use (2 measured
                                   // faster than 4 or 8: every CU requests its X at once)
-constexpr int kS1TileLd = 36;     // fp32 stride of one column of the reduction tile (32 + 4)
+constexpr int kS1TileBytes = 147456;   // LDS for the reduction tiles (8 waves x 128 x 36 fp32)
+constexpr int kS1MinWGs64 = 256;  // workgroups from which 64-token workgroups are used
 
 template <int R>
 struct Stage1Shape {
@@ -45,15 +46,24 @@ struct Stage1Shape {
 };
 
 // ---------------------------------------------------------------- stage 1 --
-template <int R>
+// MB 16-row token blocks per workgroup: 2 (32 tokens) or 4 (64 tokens, which
+// halves the sign expansion per product where the grid still fills the chip).
+template <int R, int MB>
 __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__restrict__ X, int64_t ldx,
                                                           int T, int K, uint64_t key, float c,
-                                                          uint16_t *__restrict__ P, int *__restrict__ sync,
-                                                          int n_sync) {
+                                                          uint16_t *__restrict__ P, int p_blocks,
+                                                          int *__restrict__ sync, int n_sync) {
     using Sh = Stage1Shape<R>;
     constexpr int RT = Sh::RT, NB = Sh::NB, PF = kS1Prefetch;
+    constexpr int TOK = 16 * MB;                       // tokens per workgroup
+    constexpr int kTileLd = TOK + 4;                   // fp32 stride of one column of a wave's tile
+    constexpr int kWaveTile = RT * kTileLd * 4;        // bytes of one wave's tile
+    // wave tiles LDS holds at once: all eight, or four (then waves 4..7 hand
+    // theirs to waves 0..3 first)
+    constexpr int NT = kS1Waves * kWaveTile <= kS1TileBytes ? kS1Waves : kS1Waves / 2;
+    static_assert(NT * kWaveTile <= kS1TileBytes, "reduction tiles exceed the LDS budget");
     constexpr int kTableBytes = kS1Waves * kS1Words * RT * 8;
-    constexpr int kTileBytes = kS1Waves * RT * kS1TileLd * 4;
+    constexpr int kTileBytes = NT * kWaveTile;
     // The per-wave sign-word tables during the loop, the reduction tile after it.
     __shared__ __attribute__((aligned(16))) char smem[kTableBytes > kTileBytes ? kTableBytes : kTileBytes];
     uint64_t *table = reinterpret_cast<uint64_t *>(smem);
@@ -65,9 +75,8 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
     if (blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = tid; i < n_sync; i += 64 * kS1Waves) sync[i] = 0;
     const int i16 = lane & 15, g = lane >> 4;
-    const int tb = blockIdx.x;                 // 32-token block
     const int l0 = blockIdx.y * RT;            // first sign column of the tile
-    const int t0 = tb * kS1Tokens;
+    const int t0 = blockIdx.x * TOK;
 
     // This wave's share of k, in whole 64-column word blocks.
     const int nkb = (K + 63) >> 6;
@@ -80,9 +89,9 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
     constexpr uint32_t kOob = 0x80000000u;
     const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(X), 0, static_cast<int>(static_cast<int64_t>(T) * ldx * 2), 0x00020000);
-    uint32_t row_off[2];
+    uint32_t row_off[MB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
         const int t = t0 + 16 * mb + i16;
         row_off[mb] = t < T ? static_cast<uint32_t>(static_cast<int64_t>(t) * ldx * 2) : kOob;
     }
@@ -106,17 +115,17 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     };
 
-    f32x4_t acc[2][NB];
+    f32x4_t acc[MB][NB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero_f32x4();
 
-    u32x4_t xa[PF][2];
+    u32x4_t xa[PF][MB];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) xa[p][mb] = xload(s_begin + p, mb);
+        for (int mb = 0; mb < MB; ++mb) xa[p][mb] = xload(s_begin + p, mb);
 
     const uint32_t one_pair = opaque_u32(0x3F803F80u);   // two bf16 +1.0
     int first = kb0;   // first block held in the table
@@ -144,33 +153,59 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
                     bf[nb] = signs8_to_bf16(__builtin_amdgcn_ubfe(dw, 8 * g, 8), one_pair);
                 }
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_bf16(xa[p][mb], bf[nb], acc[mb][nb]);
             }
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) xa[p][mb] = xload(s + PF, mb);
+            for (int mb = 0; mb < MB; ++mb) xa[p][mb] = xload(s + PF, mb);
         }
     }
 
     // The waves' tiles go to LDS as tile[wave][column][token] and are added
-    // in wave order. Lane (i16, g) of block (mb, nb) holds tokens
-    // 16 mb + 4 g .. +3 of column 16 nb + i16.
+    // in wave order (with four tiles held at once, wave w + 4 first adds its
+    // tile to wave w's, so the sum is (t0 + t4) + (t1 + t5) + ...). Lane
+    // (i16, g) of block (mb, nb) holds tokens 16 mb + 4 g .. +3 of column
+    // 16 nb + i16.
     __syncthreads();   // every wave is done with its word table
+    auto tile_at = [&](int w, int mb, int nb) -> f32x4_t * {
+        return reinterpret_cast<f32x4_t *>(&tile[(w * RT + 16 * nb + i16) * kTileLd + 16 * mb + 4 * g]);
+    };
+    if constexpr (NT < kS1Waves) {
+        if (wave >= NT) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            *reinterpret_cast<f32x4_t *>(&tile[(wave * RT + 16 * nb + i16) * kS1TileLd + 16 * mb + 4 * g]) =
-                acc[mb][nb];
+                for (int nb = 0; nb < NB; ++nb) *tile_at(wave - NT, mb, nb) = acc[mb][nb];
+        }
+        __syncthreads();
+        if (wave < NT) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = *tile_at(wave, mb, nb) + acc[mb][nb];
+        }
+        __syncthreads();
+    }
+    if (wave < NT) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) *tile_at(wave, mb, nb) = acc[mb][nb];
+    }
     __syncthreads();
-    // Output chunks: column q / 4, tokens 8 (q % 4) .. +7 (16 bytes of P).
-    for (int q = tid; q < RT * 4; q += 64 * kS1Waves) {
-        const int col = q >> 2, tq = 8 * (q & 3);
+    // Output chunks: column q / (TOK / 8), tokens 8 (q % (TOK / 8)) .. +7
+    // (16 bytes of P), in the P block of those tokens; blocks past the
+    // buffer (a ragged last workgroup) are not written.
+    constexpr int CPC = TOK / 8;   // chunks per column
+    for (int q = tid; q < RT * CPC; q += 64 * kS1Waves) {
+        const int col = q / CPC, tq = 8 * (q % CPC);
+        const int blk = (t0 + tq) / kS1Tokens;
+        if (blk >= p_blocks) continue;
         f32x4_t lo = zero_f32x4(), hi = zero_f32x4();
 #pragma unroll
-        for (int w = 0; w < kS1Waves; ++w) {
-            const float *src = &tile[(w * RT + col) * kS1TileLd + tq];
+        for (int w = 0; w < NT; ++w) {
+            const float *src = &tile[(w * RT + col) * kTileLd + tq];
             lo += *reinterpret_cast<const f32x4_t *>(src);
             hi += *reinterpret_cast<const f32x4_t *>(src + 4);
         }
@@ -179,7 +214,8 @@ __global__ __launch_bounds__(512) void stage1_bf16_kernel(const uint16_t *__rest
         o.y = pack_bf16x2(c * lo.z, c * lo.w);
         o.z = pack_bf16x2(c * hi.x, c * hi.y);
         o.w = pack_bf16x2(c * hi.z, c * hi.w);
-        *reinterpret_cast<u32x4_t *>(P + (static_cast<size_t>(tb) * R + l0 + col) * 32 + tq) = o;
+        *reinterpret_cast<u32x4_t *>(P + (static_cast<size_t>(blk) * R + l0 + col) * kS1Tokens +
+                                     (t0 + tq) % kS1Tokens) = o;
     }
 }
 
@@ -201,8 +237,13 @@ static hipError_t project_bf16_r(int64_t T, int64_t D, int64_t K, uint64_t key, 
     const FoldPlan f = plan_fold_bf16(T, D, R);
     uint16_t *P = static_cast<uint16_t *>(ws);
     int *sync = reinterpret_cast<int *>(static_cast<char *>(ws) + p.p_bytes + f.xbuf_bytes);
-    hipLaunchKernelGGL(stage1_bf16_kernel<R>, dim3(p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
-                       static_cast<int>(T), static_cast<int>(K), key, c, P, sync, f.sync_words);
+    // 64-token workgroups where they still give a workgroup per compute
+    // unit, else 32-token ones
+    const int wg64 = (p.t_blocks + 1) / 2;
+    const bool tall = static_cast<int64_t>(wg64) * p.col_tiles >= kS1MinWGs64;
+    auto kernel = tall ? stage1_bf16_kernel<R, 4> : stage1_bf16_kernel<R, 2>;
+    hipLaunchKernelGGL(kernel, dim3(tall ? wg64 : p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
+                       static_cast<int>(T), static_cast<int>(K), key, c, P, p.t_blocks, sync, f.sync_words);
     return hipGetLastError();
 }
 

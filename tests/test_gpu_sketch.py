@@ -55,6 +55,10 @@ BF16_CASES = [
     (130, 72, 72, 256, 1),
     (8, 8, 8, 256, 1),
     (513, 1032, 4104, 256, 1),
+    # projections in 64-token workgroups (enough of them to fill the chip),
+    # ragged: the last workgroup's second P block lies past the buffer
+    (8200, 72, 136, 256, 2),
+    (16400, 40, 72, 128, 1),
 ]
 
 
