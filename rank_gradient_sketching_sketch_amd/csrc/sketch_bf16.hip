@@ -11,8 +11,10 @@
 //   stage 2   S (+)= dY^T P  (d x r, contraction over the tokens): the fold
 //             kernel in fold_bf16.hip.
 //
-// Stage 1 design. A workgroup owns 32 tokens x 128 (or r, if smaller) sign
-// columns over the whole of k, so no partial sums leave the chip: its eight
+// Stage 1 design. A workgroup owns 32 tokens (64 where that still gives at
+// least 256 workgroups: each sign fragment then feeds four token blocks) x
+// 128 (or r, if smaller) sign columns over the whole of k, so no partial sums
+// leave the chip: its eight
 // waves (two per SIMD, so one wave's sign arithmetic overlaps the other's
 // matrix and memory work) split the k range, each accumulating the full
 // 32 x 128 tile, and add their tiles through LDS in a fixed order at the end.
