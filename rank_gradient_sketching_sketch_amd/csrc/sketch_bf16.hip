@@ -14,10 +14,10 @@
 // Stage 1 design. A workgroup owns 32 tokens (64 where that still gives at
 // least 256 workgroups: each sign fragment then feeds four token blocks) x
 // 128 (or r, if smaller) sign columns over the whole of k, so no partial sums
-// leave the chip: its eight
-// waves (two per SIMD, so one wave's sign arithmetic overlaps the other's
-// matrix and memory work) split the k range, each accumulating the full
-// 32 x 128 tile, and add their tiles through LDS in a fixed order at the end.
+// leave the chip: its eight waves (two per SIMD, so one wave's sign
+// arithmetic overlaps the other's matrix and memory work) split the k range,
+// each accumulating the whole tile, and add their tiles through LDS in a
+// fixed order at the end.
 // Sigma is never stored: each wave hashes the 64-bit sign words of its k range
 // into an LDS table (8 word blocks at a time), and every step expands one byte per lane into
 // eight bf16 +-1 values, the B operand of the MFMA. X streams straight from
