@@ -604,17 +604,26 @@ FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R) {
             p.n_tiles = by_height > kFoldWGs ? by_height : kFoldWGs;
         }
     } else {
-        // small d: tiles of 4 blocks, the tokens split so that the grid fills
-        // the compute units, keeping the exchanged partials no larger than the
-        // dY they replace and at least 4 steps per member
-        p.n_tiles = (p.nblk + 3) / 4;
-        int ns = kFoldWGs / p.n_tiles;
+        // small d: the tokens split so that the grid fills the compute units,
+        // keeping the exchanged partials no larger than the dY they replace
+        // and at least 4 steps per member; tiles of up to 10 blocks (longer
+        // dY rows per step, less P per member) where they still make a
+        // workgroup per compute unit, else tiles of 4 blocks
         const int64_t cap_bytes = T / (2 * R);
-        if (ns > cap_bytes) ns = static_cast<int>(cap_bytes);
-        if (ns > nsteps / 4) ns = nsteps / 4;
-        if (ns > kFoldMaxSplit) ns = kFoldMaxSplit;
-        if (ns < 1) ns = 1;
-        p.n_split = ns;
+        auto splits = [&](int tiles) {
+            int ns = kFoldWGs / tiles;
+            if (ns > cap_bytes) ns = static_cast<int>(cap_bytes);
+            if (ns > nsteps / 4) ns = nsteps / 4;
+            if (ns > kFoldMaxSplit) ns = kFoldMaxSplit;
+            return ns < 1 ? 1 : ns;
+        };
+        const int tall = (p.nblk + 9) / 10;
+        if (tall * splits(tall) >= kFoldWGs) {
+            p.n_tiles = tall;
+        } else {
+            p.n_tiles = (p.nblk + 3) / 4;
+        }
+        p.n_split = splits(p.n_tiles);
     }
     p.max_blocks = (p.nblk + p.n_tiles - 1) / p.n_tiles <= 5 ? 5 : 10;
     p.steps_per = (nsteps + p.n_split - 1) / p.n_split;
@@ -642,7 +651,7 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
     int *sync = reinterpret_cast<int *>(static_cast<char *>(scratch) + p.xbuf_bytes);
     auto kernel = fold_bf16_kernel<R, 5, kFoldSingle>;
     if (p.n_split > 2)
-        kernel = fold_bf16_kernel<R, 5, kFoldPartial>;   // small d: tiles of at most 4 blocks
+        kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldPartial> : fold_bf16_kernel<R, 10, kFoldPartial>;
     else if (p.n_split == 2)
         kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldPair> : fold_bf16_kernel<R, 10, kFoldPair>;
     else if (p.max_blocks == 10)

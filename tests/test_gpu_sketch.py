@@ -91,6 +91,10 @@ FOLD_SPLIT_CASES = [
     (200, 41000, 72, 32, 2),
     (257, 24008, 64, 64, 2),
     (1000, 9000, 40, 128, 1),
+    # small d in tiles of up to 10 blocks, 8 members each (32 x 8 = 256
+    # workgroups), one of them ragged in d and T
+    (1024, 5120, 64, 32, 2),
+    (1000, 5000, 72, 32, 1),
 ]
 
 
