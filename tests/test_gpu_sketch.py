@@ -95,6 +95,10 @@ FOLD_SPLIT_CASES = [
     # workgroups), one of them ragged in d and T
     (1024, 5120, 64, 32, 2),
     (1000, 5000, 72, 32, 1),
+    # small d where taller tiles would not fill the chip: 4-block tiles x 4
+    # members (the plan of the 7B stack's q/o/down at 4096 tokens), ragged in d
+    (1024, 3584, 64, 32, 1),
+    (1000, 3592, 72, 32, 1),
 ]
 
 
