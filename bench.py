@@ -181,8 +181,9 @@ def main():
     for i, m in enumerate(mats):
         m["lane"] = lanes[i % n_sketch]
         m["alane"] = lanes[i % n_apply]
-    # Pass 1 in batches: each apply stream's matrices in chunks of up to
-    # B.MAX_BATCH, one call (two launches) per chunk; a chunk of one matrix
+    # Pass 1 in batches: each apply stream's matrices in as few chunks of at
+    # most B.MAX_BATCH as hold them, of equal size (65 matrices: 5 x 13, not
+    # 4 x 16 + 1), one call (two launches) per chunk; a chunk of one matrix
     # uses the single-matrix call. Each batched matrix's sqnorm is a view of
     # its chunk's n-float output.
     batches = []
@@ -190,8 +191,10 @@ def main():
     if not args.no_batch:
         for ln in lanes[:n_apply]:
             own = [m for m in mats if m["alane"] is ln]
-            for c0 in range(0, len(own), B.MAX_BATCH):
-                chunk = own[c0:c0 + B.MAX_BATCH]
+            n_chunks = -(-len(own) // B.MAX_BATCH)
+            bounds = [len(own) * i // max(1, n_chunks) for i in range(n_chunks + 1)]
+            for c0, c1 in zip(bounds[:-1], bounds[1:]):
+                chunk = own[c0:c1]
                 if len(chunk) == 1:
                     batches.append((ln, chunk, None, None))
                     continue
