@@ -485,10 +485,29 @@ def cpu_baseline(wl, budget_s=15.0):
             flop += 2.0 * wl.tokens * wl.r * (spec.d + spec.k)
             done += 1
     total = wl.microbatches * len(wl.matrices)
-    return {"value": round(flop / spent / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(spent, 2), "cpu": cpu_model(),
-            "sample": "%d of the step's %d sketch-accumulate units (microbatch x matrix, %d tokens each), "
-                      "all rows, fp64" % (done, total, wl.tokens)}
+    out = {"value": round(flop / spent / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "seconds": round(spent, 2), "cpu": cpu_model(),
+           "sample": "%d of the step's %d sketch-accumulate units (microbatch x matrix, %d tokens each), "
+                     "all rows, fp64" % (done, total, wl.tokens)}
+    # the same oracle on one thread, for one unit (the first microbatch of the
+    # largest matrix)
+    spec = max(wl.matrices, key=lambda s: s.d * s.k)
+    X = inputs.activations(wl, spec, 0, 0).double().numpy()
+    dY = inputs.output_grads(wl, spec, 0, 0).double().numpy()
+    A = oracle.sign_matrix(0, 0, spec.matrix_id, wl.r, spec.k)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.sketch_rows(dY, oracle.project(X, A), accumulate=False)
+        one = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    out["single_thread"] = {"value": round(2.0 * wl.tokens * wl.r * (spec.d + spec.k) / one / 1e12, 6),
+                            "unit": "TFLOP/s", "seconds": round(one, 2),
+                            "sample": "one sketch-accumulate unit, %d x %d, %d tokens, all rows, fp64"
+                                      % (spec.d, spec.k, wl.tokens)}
+    return out
 
 
 if __name__ == "__main__":

@@ -47,6 +47,8 @@ def _load():
     P = ctypes.c_void_p
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_mix64.restype = u64
     lib.oracle_mix64.argtypes = [u64]
     lib.oracle_splitmix64_output.restype = u64
@@ -83,6 +85,11 @@ def _ptr(a: np.ndarray):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ hash ---

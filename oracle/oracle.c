@@ -60,6 +60,17 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Sets the threads of later OpenMP loops (for timing only; n < 1 is
+ * ignored). No arithmetic depends on it: every output element is computed
+ * by one thread in a fixed order. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------- hash --- */
 
 #define SM64_GAMMA 0x9E3779B97F4A7C15ULL
