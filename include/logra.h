@@ -40,9 +40,10 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller (except the
  *     host arrays of the step controller at the end). The library
- *     allocates nothing and is reentrant; its one piece of mutable global
- *     state is the fold's partner-wait limit (logra_set_fold_wait_limit),
- *     a process-wide setting read when a fold is launched.
+ *     allocates nothing and is reentrant; its only mutable global state
+ *     is two process-wide settings read when a kernel is launched: the
+ *     fold's partner-wait limit (logra_set_fold_wait_limit) and the sketch
+ *     concurrency hint (logra_set_sketch_concurrency).
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; results are visible after the caller
  *     synchronises the stream.
@@ -193,6 +194,24 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
  * Errors: none.
  */
 logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous);
+
+/*
+ * logra_set_sketch_concurrency -- how many independent sketch calls
+ * (logra_sketch_accumulate / logra_sketch_project of different matrices)
+ * the caller keeps in flight at once on separate streams; default 1. The
+ * projection sizes its workgroups for a 1/n share of the chip: with a larger
+ * n it uses fewer, taller workgroups (64 tokens each, never fewer than 128
+ * of them) that expand each sign fragment for more tokens, which is faster
+ * when other streams fill the rest of the chip and slower when the call has
+ * it to itself. Results stay
+ * within the same tolerance of the oracle (the summation order of the
+ * projection differs between the two shapes). Process-wide; applies to
+ * projections launched after the call.
+ * previous: host, may be NULL; receives the value in force before the call.
+ * Not an operation of the pages: a scheduling hint of this implementation.
+ * Errors: INVALID_ARGUMENT for n < 1 or n > 256 (nothing changes).
+ */
+logra_status logra_set_sketch_concurrency(int32_t n, int32_t *previous);
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs

@@ -82,6 +82,8 @@ def load_library():
     lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, P]
     lib.logra_set_fold_wait_limit.restype = i32
     lib.logra_set_fold_wait_limit.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.logra_set_sketch_concurrency.restype = i32
+    lib.logra_set_sketch_concurrency.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
@@ -176,6 +178,16 @@ def logra_set_fold_wait_limit(polls: int) -> int:
     prev = ctypes.c_int32(0)
     _check(load_library().logra_set_fold_wait_limit(int(polls), ctypes.byref(prev)),
            "logra_set_fold_wait_limit")
+    return int(prev.value)
+
+
+def logra_set_sketch_concurrency(n: int) -> int:
+    """Independent sketch calls kept in flight on separate streams (the
+    projection sizes its workgroups for that share of the chip); returns the
+    previous value. Process-wide."""
+    prev = ctypes.c_int32(0)
+    _check(load_library().logra_set_sketch_concurrency(int(n), ctypes.byref(prev)),
+           "logra_set_sketch_concurrency")
     return int(prev.value)
 
 

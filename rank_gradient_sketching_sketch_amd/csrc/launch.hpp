@@ -37,6 +37,9 @@ FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
 // Sets the polls a fold member makes for its partner before it gives up and
 // writes its rows as NaN; returns the previous limit. Negative: give up at once.
 int set_fold_spin_limit(int polls);
+// Sets how many independent sketch calls run at once (the projection sizes
+// its workgroups for that share of the chip); returns the previous value.
+int set_sketch_concurrency(int n);
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, hipStream_t st);

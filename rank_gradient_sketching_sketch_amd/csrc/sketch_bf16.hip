@@ -37,7 +37,18 @@ constexpr int kS1Words = 8;       // sign-word blocks (64 columns of k each) has
 constexpr int kS1Prefetch = 2;    // steps of X held in registers ahead of use (2 measured
                                   // faster than 4 or 8: every CU requests its X at once)
 constexpr int kS1TileBytes = 147456;   // LDS for the reduction tiles (8 waves x 128 x 36 fp32)
-constexpr int kS1MinWGs64 = 256;  // workgroups from which 64-token workgroups are used
+constexpr int kS1MinWGs64 = 256;  // workgroups (times the concurrency) from which 64-token ones are used
+
+// Independent sketch calls the caller keeps in flight on separate streams
+// (process-wide; logra_set_sketch_concurrency). The projection picks its
+// workgroup shape for a 1/n share of the chip.
+static int g_sketch_concurrency = 1;
+
+int set_sketch_concurrency(int n) {
+    const int prev = g_sketch_concurrency;
+    g_sketch_concurrency = n;
+    return prev;
+}
 
 template <int R>
 struct Stage1Shape {
@@ -240,9 +251,12 @@ static hipError_t project_bf16_r(int64_t T, int64_t D, int64_t K, uint64_t key, 
     uint16_t *P = static_cast<uint16_t *>(ws);
     int *sync = reinterpret_cast<int *>(static_cast<char *>(ws) + p.p_bytes + f.xbuf_bytes);
     // 64-token workgroups where they still give a workgroup per compute
-    // unit, else 32-token ones
+    // unit of this call's share of the chip, and never fewer than half a
+    // chip's worth of them (with four streams, 64 workgroups of 64 tokens
+    // lost to 128 of 32), else 32-token ones
     const int wg64 = (p.t_blocks + 1) / 2;
-    const bool tall = static_cast<int64_t>(wg64) * p.col_tiles >= kS1MinWGs64;
+    const int64_t n64 = static_cast<int64_t>(wg64) * p.col_tiles;
+    const bool tall = n64 * g_sketch_concurrency >= kS1MinWGs64 && 2 * n64 >= kS1MinWGs64;
     auto kernel = tall ? stage1_bf16_kernel<R, 4> : stage1_bf16_kernel<R, 2>;
     hipLaunchKernelGGL(kernel, dim3(tall ? wg64 : p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
                        static_cast<int>(T), static_cast<int>(K), key, c, P, p.t_blocks, sync, f.sync_words);

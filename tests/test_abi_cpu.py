@@ -58,6 +58,19 @@ def test_fold_wait_limit_round_trip(lib):
         assert B.logra_set_fold_wait_limit(prev) == 7
 
 
+def test_sketch_concurrency_round_trip(lib):
+    # host-side setting only: default 1, previous value returned, range checked
+    from rank_gradient_sketching_sketch_amd import binding as B
+    prev = B.logra_set_sketch_concurrency(4)
+    try:
+        assert prev == 1
+        assert lib.logra_set_sketch_concurrency(0, None) == 1      # INVALID_ARGUMENT
+        assert lib.logra_set_sketch_concurrency(257, None) == 1
+        assert B.logra_set_sketch_concurrency(2) == 4               # unchanged by the errors
+    finally:
+        assert B.logra_set_sketch_concurrency(prev) == 2
+
+
 def _m(d=64, k=128, r=32):
     from rank_gradient_sketching_sketch_amd import binding as B
     return B.MatrixDesc(d, k, r, 0, 0, 0)

@@ -172,6 +172,27 @@ def test_fold_wait_timeout_writes_nan_and_recovers():
     assert torch.equal(S, S_ref)
 
 
+@pytest.mark.parametrize("n", [1, 4])
+def test_sketch_concurrency_hint_keeps_parity(n):
+    # With a concurrency of 4 the projection of 4040 tokens runs in 64-token
+    # workgroups (64 x 2: the last one has a partial P block and one past the
+    # buffer), with 1 in 32-token ones; both match the oracle to the same
+    # tolerance.
+    dev = device()
+    T, d, k, r = 4040, 264, 200, 256
+    say("sketch concurrency", n, T, d, k, r)
+    m = B.MatrixDesc(d, k, r, seed=9, step=n, matrix_id=d)
+    X, dY = inputs.random_case(4242 + n, T, d, k, dtype=torch.bfloat16, dy_std=1e-2, outlier_cols=2)
+    prev = B.logra_set_sketch_concurrency(n)
+    try:
+        S = _run_sketch(m, [X], [dY], dev)
+    finally:
+        assert B.logra_set_sketch_concurrency(prev) == n
+    err = rownorm_err(to_f64(S), _ref_sketch(m, [X], [dY]))
+    say("  S rownorm err %.3e" % err)
+    assert err < BF16_TOL
+
+
 F32_CASES = [
     (128, 256, 512, 32, 4),     # the tiny fp32 workload's shape
     (77, 45, 130, 20, 2),
