@@ -171,6 +171,7 @@ def main():
     n_apply = max(1, min(n_apply, len(mats)))
     # the projections share the chip with the other sketch streams' work
     B.logra_set_sketch_concurrency(n_sketch)
+    B.logra_set_apply_concurrency(n_apply)
     n_streams = max(n_sketch, n_apply)
     main = torch.cuda.current_stream()
     lanes = []
@@ -405,7 +406,7 @@ def main():
                    "microbatch_inputs": sum(t.numel() * t.element_size()
                                             for t in list(xbuf.values()) + list(ybuf.values())),
                    "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes)) + batch_ws_bytes},
-        "streams": {"sketch": n_sketch, "apply": n_apply, "sketch_concurrency": n_sketch,
+        "streams": {"sketch": n_sketch, "apply": n_apply, "sketch_concurrency": n_sketch, "apply_concurrency": n_apply,
                     "pass1_batches": sum(1 for b in batches if b[2] is not None)},
         "controller": {"fisher_scale": KL_PHI,
                        "budget": [kl_budget.delta_start, kl_budget.delta_end, kl_budget.anneal_steps],

@@ -41,9 +41,10 @@
  *   - All data pointers are DEVICE pointers owned by the caller (except the
  *     host arrays of the step controller at the end). The library
  *     allocates nothing and is reentrant; its only mutable global state
- *     is two process-wide settings read when a kernel is launched: the
+ *     is three process-wide settings read when a kernel is launched: the
  *     fold's partner-wait limit (logra_set_fold_wait_limit) and the sketch
- *     concurrency hint (logra_set_sketch_concurrency).
+ *     and apply concurrency hints (logra_set_sketch_concurrency,
+ *     logra_set_apply_concurrency).
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; results are visible after the caller
  *     synchronises the stream.
@@ -212,6 +213,21 @@ logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous);
  * Errors: INVALID_ARGUMENT for n < 1 or n > 256 (nothing changes).
  */
 logra_status logra_set_sketch_concurrency(int32_t n, int32_t *previous);
+
+/*
+ * logra_set_apply_concurrency -- how many apply calls (logra_rowadam_apply
+ * of different matrices) the caller keeps in flight at once on separate
+ * streams; default 1. With n > 1 the bf16 pass 2 of a large matrix (at
+ * least 1024 tiles of 256 rows x 64 columns) deals its work over 128
+ * workgroups instead of 256 (each walks a longer range of W), which is
+ * faster when other streams fill the rest of the chip and slower when the
+ * call has it to itself. Results stay within the same tolerance of the
+ * oracle. Process-wide; applies to launches after the call.
+ * previous: host, may be NULL; receives the value in force before the call.
+ * Not an operation of the pages: a scheduling hint of this implementation.
+ * Errors: INVALID_ARGUMENT for n < 1 or n > 256 (nothing changes).
+ */
+logra_status logra_set_apply_concurrency(int32_t n, int32_t *previous);
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs

@@ -84,6 +84,8 @@ def load_library():
     lib.logra_set_fold_wait_limit.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.logra_set_sketch_concurrency.restype = i32
     lib.logra_set_sketch_concurrency.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.logra_set_apply_concurrency.restype = i32
+    lib.logra_set_apply_concurrency.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
@@ -188,6 +190,16 @@ def logra_set_sketch_concurrency(n: int) -> int:
     prev = ctypes.c_int32(0)
     _check(load_library().logra_set_sketch_concurrency(int(n), ctypes.byref(prev)),
            "logra_set_sketch_concurrency")
+    return int(prev.value)
+
+
+def logra_set_apply_concurrency(n: int) -> int:
+    """Independent apply calls kept in flight on separate streams (pass 2
+    sizes its grid for that share of the chip); returns the previous value.
+    Process-wide."""
+    prev = ctypes.c_int32(0)
+    _check(load_library().logra_set_apply_concurrency(int(n), ctypes.byref(prev)),
+           "logra_set_apply_concurrency")
     return int(prev.value)
 
 

@@ -71,6 +71,13 @@ logra_status logra_set_sketch_concurrency(int32_t n, int32_t *previous) {
     return LOGRA_OK;
 }
 
+logra_status logra_set_apply_concurrency(int32_t n, int32_t *previous) {
+    if (n < 1 || n > 256) return LOGRA_ERR_INVALID_ARGUMENT;
+    const int prev = logra::set_apply_concurrency(n);
+    if (previous) *previous = prev;
+    return LOGRA_OK;
+}
+
 logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stream) {
     if (!matrix_ok(m) || !words) return LOGRA_ERR_INVALID_ARGUMENT;
     if (m->r > (1ll << 20)) return LOGRA_ERR_UNSUPPORTED;

@@ -46,6 +46,25 @@ constexpr int kApplyRowsMax = 256;     // rows of W per row tile, most (32 per w
 constexpr int kApplyWaves = 8;
 constexpr int kApplyCols = 64;         // columns per column tile (one sign word)
 constexpr int kApplyWGs = 256;         // workgroups (one per compute unit)
+
+// Apply calls the caller keeps in flight at once on separate streams
+// (process-wide; logra_set_apply_concurrency). With more than one, pass 2
+// of a large matrix (at least kConcurrentMinUnits 256-row units) deals its
+// units over half as many workgroups, which then walk longer ranges while
+// the other streams fill the rest of the chip; smaller matrices measured
+// slower that way and keep the full grid.
+constexpr int64_t kConcurrentMinUnits = 1024;
+static int g_apply_concurrency = 1;
+
+int set_apply_concurrency(int n) {
+    const int prev = g_apply_concurrency;
+    g_apply_concurrency = n;
+    return prev;
+}
+
+static int apply_wgs(int64_t units256) {
+    return g_apply_concurrency > 1 && units256 >= kConcurrentMinUnits ? kApplyWGs / 2 : kApplyWGs;
+}
 constexpr int kTallTileUnitsPerWG = 4;  // 256-row units per workgroup from which 256-row tiles are used
 constexpr int kStagePitch = 144;       // bytes per staged row of a wave's updated bf16 block
 
@@ -348,12 +367,12 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
 }
 
 template <int R, int RB>
-static hipError_t rowadam_rb(const ApplyArgs &a, hipStream_t st) {
+static hipError_t rowadam_rb(const ApplyArgs &a, int wgs, hipStream_t st) {
     constexpr int rows = 128 * RB;
     const int n_rt = static_cast<int>((a.D + rows - 1) / rows);
     const int n_ct = static_cast<int>((a.K + kApplyCols - 1) / kApplyCols);
     const int n_units = n_rt * n_ct;
-    const int grid = n_units < kApplyWGs ? n_units : kApplyWGs;
+    const int grid = n_units < wgs ? n_units : wgs;
     if (a.w_bf16)
         hipLaunchKernelGGL((rowadam_bf16_kernel<R, true, RB>), dim3(grid), dim3(64 * kApplyWaves), 0, st, a, n_ct,
                            n_units);
@@ -369,8 +388,9 @@ static hipError_t rowadam_rb(const ApplyArgs &a, hipStream_t st) {
 template <int R>
 static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
     const int64_t units256 = ((a.D + kApplyRowsMax - 1) / kApplyRowsMax) * ((a.K + kApplyCols - 1) / kApplyCols);
-    if (units256 >= static_cast<int64_t>(kTallTileUnitsPerWG) * kApplyWGs) return rowadam_rb<R, 2>(a, st);
-    return rowadam_rb<R, 1>(a, st);
+    const int wgs = apply_wgs(units256);
+    if (units256 >= static_cast<int64_t>(kTallTileUnitsPerWG) * wgs) return rowadam_rb<R, 2>(a, wgs, st);
+    return rowadam_rb<R, 1>(a, wgs, st);
 }
 
 hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st) {

@@ -40,6 +40,9 @@ int set_fold_spin_limit(int polls);
 // Sets how many independent sketch calls run at once (the projection sizes
 // its workgroups for that share of the chip); returns the previous value.
 int set_sketch_concurrency(int n);
+// Sets how many apply calls run at once (pass 2 sizes its grid for that);
+// returns the previous value.
+int set_apply_concurrency(int n);
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, hipStream_t st);

@@ -71,6 +71,17 @@ def test_sketch_concurrency_round_trip(lib):
         assert B.logra_set_sketch_concurrency(prev) == 2
 
 
+def test_apply_concurrency_round_trip(lib):
+    from rank_gradient_sketching_sketch_amd import binding as B
+    prev = B.logra_set_apply_concurrency(3)
+    try:
+        assert prev == 1
+        assert lib.logra_set_apply_concurrency(0, None) == 1      # INVALID_ARGUMENT
+        assert B.logra_set_apply_concurrency(2) == 3
+    finally:
+        assert B.logra_set_apply_concurrency(prev) == 2
+
+
 def _m(d=64, k=128, r=32):
     from rank_gradient_sketching_sketch_amd import binding as B
     return B.MatrixDesc(d, k, r, 0, 0, 0)

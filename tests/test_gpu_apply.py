@@ -91,6 +91,32 @@ def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
         assert ok
 
 
+@pytest.mark.parametrize("d,k,r", [(1000, 4104, 256), (4608, 3592, 256), (8200, 136, 256)])
+def test_apply_concurrency_hint_keeps_parity(d, k, r):
+    # With an apply concurrency of 3 pass 2 of a matrix of at least 1024
+    # 256 x 64 tiles (4608 x 3592: 18 x 57) runs on 128 workgroups, and in
+    # 256-row tiles from half as many units; smaller ones keep the default
+    # grid. W matches the oracle to the same bound either way.
+    dev = device()
+    say("apply concurrency 3", d, k, r)
+    m = B.MatrixDesc(d, k, r, seed=6, step=d, matrix_id=k)
+    S, v, W = _state(7 * d + k, d, k, r)
+    W = W.to(torch.bfloat16)
+    lr, scale, beta2, eps = 1e-3, 0.8, 0.999, 1e-8
+    prev = B.logra_set_apply_concurrency(3)
+    try:
+        _, _, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, W, lr, scale, beta2, eps, dev)
+    finally:
+        assert B.logra_set_apply_concurrency(prev) == 3
+    A = oracle.sign_matrix(6, d, k, r, k)
+    ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
+                              beta2=f32(beta2), eps=f32(eps), lr=f32(lr), scale=f32(scale))
+    assert rel_err(v_new.double().numpy(), ref["v_new"]) < BF16_TOL
+    ok, worst = bf16_w_check(W_new.double().numpy(), ref["W_new"], W.double().numpy())
+    say("  bf16 W worst error / allowed %.3f" % worst)
+    assert ok
+
+
 @pytest.mark.parametrize("d,k,r", [(256, 512, 32), (45, 130, 20), (300, 65, 1), (64, 256, 100),
                                    (17, 9, 1024)])
 def test_apply_f32_compute_matches_oracle(d, k, r):
