@@ -85,6 +85,9 @@ def parse():
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
+    ap.add_argument("--prepare", action="store_true",
+                    help="one-matrix workloads: build pass 1's Gram matrix ahead, on a side stream "
+                         "during the sketch (logra_sqnorm_prepare), instead of inside pass 1")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time torch.mm (the vendor GEMM) on the fold's contraction and on the "
                          "dense dY^T X it replaces, for context")
@@ -208,6 +211,14 @@ def main():
                     [B.MatrixDesc(m["spec"].d, m["spec"].k, r) for m in chunk], code)
                 batch_ws_bytes += wsb
                 batches.append((ln, chunk, sq, torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)))
+    # --prepare: a one-matrix workload builds pass 1's Gram matrix (it
+    # depends only on the step's signs) ahead, on a side stream while the
+    # sketch runs, into the workspace pass 1 then reads. Off by default: it
+    # took about 4 us off pass 1 but cost the sketch about 3 %.
+    prep_stream = None
+    if len(mats) == 1 and code == B.LOGRA_BF16 and args.prepare and not args.no_batch:
+        prep_stream = torch.cuda.Stream(device=dev)
+
     # Microbatch buffers: every microbatch has its own; layer stacks rotate
     # two sets of per-layer inputs (even and odd layers), which keeps a
     # 28- or 64-layer step within memory while consecutive layers still read
@@ -274,18 +285,27 @@ def main():
         # sketch takes each microbatch in turn
         e0 = ev() if timed else None
         fork()
+        if prep_stream is not None:
+            prep_stream.wait_stream(main)
+            B.logra_sqnorm_prepare(mats[0]["desc"], code, mats[0]["alane"]["sq_ws"], prep_stream)
         for mb in range(nmb):
             for m in mats:
                 sketch_calls(step, m, mb, "both")
         join()
+        if prep_stream is not None:
+            main.wait_stream(prep_stream)
         e1 = ev() if timed else None
         fork()
         if batches:
             for ln, chunk, sq, bws in batches:
                 if sq is None:
                     m = chunk[0]
-                    B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
-                                          m["sq"], None, ln["sq_ws"], ln["stream"])
+                    if prep_stream is not None:
+                        B.logra_update_sqnorm_prepared(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps,
+                                                       m["v_new"], m["sq"], ln["sq_ws"], None, ln["stream"])
+                    else:
+                        B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
+                                              m["sq"], None, ln["sq_ws"], ln["stream"])
                 else:
                     B.logra_update_sqnorm_batch([m["desc"] for m in chunk], code, [m["S"] for m in chunk],
                                                 [m["v"] for m in chunk], wl.beta2, wl.eps,
@@ -407,7 +427,8 @@ def main():
                                             for t in list(xbuf.values()) + list(ybuf.values())),
                    "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes)) + batch_ws_bytes},
         "streams": {"sketch": n_sketch, "apply": n_apply, "sketch_concurrency": n_sketch, "apply_concurrency": n_apply,
-                    "pass1_batches": sum(1 for b in batches if b[2] is not None)},
+                    "pass1_batches": sum(1 for b in batches if b[2] is not None),
+                    "pass1_prepared": prep_stream is not None},
         "controller": {"fisher_scale": KL_PHI,
                        "budget": [kl_budget.delta_start, kl_budget.delta_end, kl_budget.anneal_steps],
                        "kl_pred_last_step": ctl_log[-1][1], "gamma_last_step": ctl_log[-1][2],

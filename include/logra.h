@@ -269,6 +269,33 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype,
                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * logra_sqnorm_prepare / logra_update_sqnorm_prepared -- logra_update_sqnorm
+ * in two calls. Pass 1 first builds the r x r Gram matrix of the step's signs
+ * (Sigma Sigma^T, exact integers), which depends only on (seed, step,
+ * matrix_id, k, r) and not on S; prepare writes it into the workspace, so a
+ * caller can run it early, for example on another stream while the sketch
+ * is still accumulating; update_sqnorm_prepared then runs the rest of pass 1
+ * reading it. The pair is logra_update_sqnorm: same kernels, bit-identical
+ * outputs.
+ *   prepare: m, compute_dtype and ws as for logra_update_sqnorm (the same m,
+ *            including d, which fixes the workspace layout). The fp32 path
+ *            has nothing to prepare and launches nothing.
+ *   prepared: the arguments of logra_update_sqnorm; ws must hold the Gram
+ *            matrix that prepare wrote for this m, and the caller orders the
+ *            two (same stream, or an event) and does not use ws for
+ *            anything else in between.
+ * Errors: as logra_update_sqnorm (prepare: INVALID_ARGUMENT, UNSUPPORTED,
+ *   WORKSPACE, HIP).
+ */
+logra_status logra_sqnorm_prepare(const logra_matrix *m, int compute_dtype,
+                                  void *ws, size_t ws_bytes, void *stream);
+logra_status logra_update_sqnorm_prepared(const logra_matrix *m, int compute_dtype,
+                                          const float *S, const float *v,
+                                          float beta2, float eps,
+                                          float *v_new, float *rowsq, float *sqnorm,
+                                          void *ws, size_t ws_bytes, void *stream);
+
+/*
  * logra_update_sqnorm_batch -- pass 1 of n matrices in one call (1 <= n <=
  * LOGRA_MAX_BATCH), exactly what n calls of logra_update_sqnorm would give
  * (same arithmetic, bit-identical outputs), with two kernel launches in all

@@ -13,6 +13,7 @@ __all__ = [
     "logra_sketch_project", "logra_sketch_fold", "logra_set_fold_wait_limit",
     "logra_set_sketch_concurrency", "logra_set_apply_concurrency",
     "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
+    "logra_sqnorm_prepare", "logra_update_sqnorm_prepared",
     "logra_sqnorm_batch_workspace_bytes", "logra_update_sqnorm_batch",
     "logra_kl_budget_at", "logra_kl_step_scale", "KLBudget",
     "LograError", "MatrixDesc", "library_path", "load_library",

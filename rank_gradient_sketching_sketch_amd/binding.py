@@ -90,6 +90,10 @@ def load_library():
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
     lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
+    lib.logra_update_sqnorm_prepared.restype = i32
+    lib.logra_update_sqnorm_prepared.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
+    lib.logra_sqnorm_prepare.restype = i32
+    lib.logra_sqnorm_prepare.argtypes = [D, i32, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
     lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, i32, i64, f32, f32, f32, P]
     PP = ctypes.POINTER(ctypes.c_void_p)
@@ -237,6 +241,25 @@ def logra_update_sqnorm(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: t
         ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
         _ptr(v_new), _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws_bytes, _stream(stream)),
         "logra_update_sqnorm")
+
+
+def logra_sqnorm_prepare(m: MatrixDesc, compute_dtype: int, ws: torch.Tensor, stream=None) -> None:
+    """First half of pass 1: the Gram matrix of the step's signs into ws."""
+    _check(load_library().logra_sqnorm_prepare(
+        ctypes.byref(m), int(compute_dtype), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "logra_sqnorm_prepare")
+
+
+def logra_update_sqnorm_prepared(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
+                                 beta2: float, eps: float, v_new: torch.Tensor, sqnorm: torch.Tensor,
+                                 ws: torch.Tensor, rowsq: Optional[torch.Tensor] = None,
+                                 stream=None) -> None:
+    """Second half of pass 1, reading the Gram matrix logra_sqnorm_prepare
+    left in ws; together they are logra_update_sqnorm."""
+    _check(load_library().logra_update_sqnorm_prepared(
+        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
+        _ptr(v_new), _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "logra_update_sqnorm_prepared")
 
 
 def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v_new: torch.Tensor,

@@ -223,10 +223,48 @@ static ApplyArgs base_args(const logra_matrix *m, const float *S, float beta2, f
     return a;
 }
 
+static logra_status update_sqnorm_parts(const logra_matrix *m, int compute_dtype, const float *S,
+                                        const float *v, float beta2, float eps, float *v_new,
+                                        float *rowsq, float *sqnorm, void *ws, size_t ws_bytes,
+                                        void *stream, int parts);
+
 logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const float *S,
                                  const float *v, float beta2, float eps, float *v_new,
                                  float *rowsq, float *sqnorm, void *ws, size_t ws_bytes,
                                  void *stream) {
+    return update_sqnorm_parts(m, compute_dtype, S, v, beta2, eps, v_new, rowsq, sqnorm, ws, ws_bytes, stream,
+                               kSqnormGram | kSqnormRows);
+}
+
+logra_status logra_update_sqnorm_prepared(const logra_matrix *m, int compute_dtype, const float *S,
+                                          const float *v, float beta2, float eps, float *v_new,
+                                          float *rowsq, float *sqnorm, void *ws, size_t ws_bytes,
+                                          void *stream) {
+    return update_sqnorm_parts(m, compute_dtype, S, v, beta2, eps, v_new, rowsq, sqnorm, ws, ws_bytes, stream,
+                               kSqnormRows);
+}
+
+logra_status logra_sqnorm_prepare(const logra_matrix *m, int compute_dtype, void *ws, size_t ws_bytes,
+                                  void *stream) {
+    if (!matrix_ok(m)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (compute_dtype == LOGRA_BF16) {
+        if (!bf16_rank_ok(m->r) || m->k % 8) return LOGRA_ERR_UNSUPPORTED;
+    } else if (compute_dtype == LOGRA_F32) {
+        if (m->r > 1024) return LOGRA_ERR_UNSUPPORTED;
+    } else {
+        return LOGRA_ERR_UNSUPPORTED;
+    }
+    const size_t need = sqnorm_ws_bytes(m, compute_dtype);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    if (compute_dtype != LOGRA_BF16) return LOGRA_OK;   // the fp32 pass has nothing to prepare
+    ApplyArgs a = base_args(m, nullptr, 0.f, 0.f);
+    return from_hip(launch_sqnorm_bf16(a, ws, static_cast<hipStream_t>(stream), kSqnormGram));
+}
+
+static logra_status update_sqnorm_parts(const logra_matrix *m, int compute_dtype, const float *S,
+                                        const float *v, float beta2, float eps, float *v_new,
+                                        float *rowsq, float *sqnorm, void *ws, size_t ws_bytes,
+                                        void *stream, int parts) {
     logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
     if (stt != LOGRA_OK) return stt;
     if (!v || !v_new || !sqnorm || v_new == v) return LOGRA_ERR_INVALID_ARGUMENT;
@@ -238,7 +276,7 @@ logra_status logra_update_sqnorm(const logra_matrix *m, int compute_dtype, const
     a.v_new_out = v_new;
     a.rowsq_out = rowsq;
     a.sqnorm = sqnorm;
-    if (compute_dtype == LOGRA_BF16) return from_hip(launch_sqnorm_bf16(a, ws, st));
+    if (compute_dtype == LOGRA_BF16) return from_hip(launch_sqnorm_bf16(a, ws, st, parts));
     a.partials = static_cast<float *>(ws);
     if (launch_apply_f32(0, a, st) != hipSuccess) return LOGRA_ERR_HIP;
     return from_hip(launch_sqnorm_final(a.partials, apply_blocks_f32(m->d), sqnorm, st));

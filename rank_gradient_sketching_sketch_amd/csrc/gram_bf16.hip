@@ -275,17 +275,19 @@ SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
 }
 
 template <int R>
-static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, hipStream_t st) {
+static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, int parts, hipStream_t st) {
     const SqnormPlan p = plan_sqnorm_bf16(a.D, a.K, R);
     char *base = static_cast<char *>(ws);
     float *partials = reinterpret_cast<float *>(base);
     uint16_t *M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
     int *counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
     const int K = static_cast<int>(a.K);
-    hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter);
-    hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
-                       static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out, partials,
-                       p.rows_per_block / 16, counter, a.sqnorm);
+    if (parts & kSqnormGram)
+        hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter);
+    if (parts & kSqnormRows)
+        hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
+                           static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out,
+                           partials, p.rows_per_block / 16, counter, a.sqnorm);
     return hipGetLastError();
 }
 
@@ -308,12 +310,12 @@ hipError_t launch_sqnorm_batch_bf16(int R, const SqnormBatch &b, hipStream_t st)
     }
 }
 
-hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st) {
+hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st, int parts) {
     switch (a.R) {
-    case 32: return sqnorm_r<32>(a, ws, st);
-    case 64: return sqnorm_r<64>(a, ws, st);
-    case 128: return sqnorm_r<128>(a, ws, st);
-    case 256: return sqnorm_r<256>(a, ws, st);
+    case 32: return sqnorm_r<32>(a, ws, parts, st);
+    case 64: return sqnorm_r<64>(a, ws, parts, st);
+    case 128: return sqnorm_r<128>(a, ws, parts, st);
+    case 256: return sqnorm_r<256>(a, ws, parts, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -121,7 +121,10 @@ hipError_t launch_sqnorm_batch_bf16(int R, const SqnormBatch &b, hipStream_t st)
 
 // bf16 compute: pass 1 (Gram form, writes v', rowsq and sqnorm) and pass 2
 // (RowAdam update of W from S and v').
-hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st);
+// Pass 1 in its two kernels: the Gram matrix of the step's signs (depends
+// only on the key, k and r) and the row pass that reads it.
+constexpr int kSqnormGram = 1, kSqnormRows = 2;
+hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st, int parts = kSqnormGram | kSqnormRows);
 hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st);
 // fp32 compute: mode 0 = pass 1 (rowsq + partials), mode 1 = pass 2 (W and v).
 hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);

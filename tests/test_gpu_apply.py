@@ -91,6 +91,35 @@ def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
         assert ok
 
 
+@pytest.mark.parametrize("d,k,r", [(1000, 4104, 256), (200, 520, 64), (8200, 136, 32)])
+def test_prepared_pass1_equals_one_call(d, k, r):
+    # The Gram matrix built ahead on a second stream (ordered by an event),
+    # then the rest of pass 1: bit-identical to logra_update_sqnorm.
+    dev = device()
+    say("pass 1 prepared", d, k, r)
+    m = B.MatrixDesc(d, k, r, seed=8, step=d, matrix_id=r)
+    S, v, _ = _state(11 * d + r, d, k, r)
+    S, v = S.to(dev), v.to(dev)
+    outs = []
+    for prepared in (False, True):
+        v_new = torch.empty(d, device=dev)
+        rowsq = torch.empty(d, device=dev)
+        sq = torch.empty(1, device=dev)
+        ws = torch.empty(B.logra_sqnorm_workspace_bytes(m, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+        if prepared:
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream())
+            B.logra_sqnorm_prepare(m, B.LOGRA_BF16, ws, side)
+            torch.cuda.current_stream().wait_stream(side)
+            B.logra_update_sqnorm_prepared(m, B.LOGRA_BF16, S, v, 0.999, 1e-8, v_new, sq, ws, rowsq)
+        else:
+            B.logra_update_sqnorm(m, B.LOGRA_BF16, S, v, 0.999, 1e-8, v_new, sq, rowsq, ws)
+        torch.cuda.synchronize()
+        outs.append((v_new.cpu(), rowsq.cpu(), sq.cpu()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("d,k,r", [(1000, 4104, 256), (4608, 3592, 256), (8200, 136, 256)])
 def test_apply_concurrency_hint_keeps_parity(d, k, r):
     # With an apply concurrency of 3 pass 2 of a matrix of at least 1024
