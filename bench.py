@@ -1,30 +1,36 @@
 """Benchmark of the LoGRA sketch-accumulate + RowAdam-apply path on one GPU.
 
-One step = every microbatch of the step folded into the sketch
-(logra_sketch_project + logra_sketch_fold, i.e. logra_sketch_accumulate),
+One step (rank_gradient_sketching_sketch_amd.step.Step) = every microbatch of
+the step folded into the sketch (logra_sketch_project + logra_sketch_fold),
 pass 1 (logra_update_sqnorm, v -> v') for every matrix, one device-to-host
 read of the sqnorms for the step controller (the library's host controller
 runs on them and its decision is reported; the update uses the workload's
 drawn scale), pass 2 (logra_rowadam_apply) for every matrix, and the swap of
-v and v'. Inputs are synthetic and already resident in HBM; each microbatch of
-a step has its own buffers, so the inputs of one step (about 3 GB in the
-default workload) stream through the 256 MB last-level cache.
+v and v'. Inputs are synthetic and already resident in HBM when the timed
+region starts: the one-matrix workloads draw fresh X and dY for every step
+and microbatch (all of them generated before timing), the layer stacks
+rotate two sets per shape.
 
 Prints one JSON line. value = sketch-accumulate TFLOP/s (algorithmic
 2*T*r*(d+k) per microbatch call, over the HIP-event time of each step's
 sketch phase, one event pair per phase); the same line carries the
 RowAdam-apply GB/s (passes 1 and 2, the device-to-host read excluded), the
-roofline of the dominant kernel (the stage-2 fold, its average launch
-duration from a back-to-back run of the step's fold calls after the timed
-steps) and the CPU oracle timed on a bounded sample of the same workload.
+roofline of the dominant kernel (the stage-2 fold: an event pair around one
+accumulating fold of every timed step, on the stream it runs on), its HBM
+traffic from the committed profiler counters (when they were taken on the
+current fold sources), and the CPU oracle timed on a bounded sample of the
+same workload. Exits with status 3 if any fold workgroup gave up waiting for
+its partner (its rows would be NaN).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -35,16 +41,19 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of roofline"
-# HBM bytes per fold launch measured with rocprofv3 counters (FETCH_SIZE x 2
-# + WRITE_SIZE x 1, the factors a plain device copy gives), per workload; see
-# profiles/hbm_traffic_qwen7b_up.md. Only valid for the fold kernel as it was
-# when the counters were taken.
-FOLD_TRAFFIC_BYTES = {"qwen7b_up": (102539 * 2 + 37940) * 1024}
+# Sources that define the fold kernel: its HBM counters are reported only
+# while these are unchanged since the counters were taken.
+FOLD_SOURCES = ("rank_gradient_sketching_sketch_amd/csrc/fold_bf16.hip",
+                "rank_gradient_sketching_sketch_amd/csrc/common.hpp",
+                "rank_gradient_sketching_sketch_amd/csrc/launch.hpp")
 # Predicted-KL controller run on every step's sqnorms and reported: an
 # isotropic Fisher of scale 1 and a budget annealed from 1e-3 to 1e-4 nats
 # over 1000 steps (the pages give no values). The update itself uses the
 # workload's drawn scale.
 KL_PHI = 1.0
+# Device memory the one-matrix workloads may spend on fresh per-step inputs
+# (beyond that, step input sets are reused in rotation).
+INPUT_BUDGET_BYTES = 120 << 30
 
 
 def sketch_flop_per_step(wl):
@@ -53,23 +62,55 @@ def sketch_flop_per_step(wl):
     return sum(2.0 * wl.tokens * wl.r * (s.d + s.k) for s in wl.matrices) * wl.microbatches
 
 
+def fold_bytes_per_launch(T, d, r, accumulate):
+    """Algorithmic bytes of one fold: dY and P read, S written, and S also
+    read when the fold accumulates."""
+    return 2 * T * d + 2 * T * r + 4 * d * r * (2 if accumulate else 1)
+
+
 def fold_bytes_per_step(wl):
-    """Algorithmic bytes of one step's folds: dY and P read, S written, and S
-    also read when the fold accumulates (every microbatch but the first)."""
-    T, r = wl.tokens, wl.r
-    total = 0.0
-    for s in wl.matrices:
-        for mb in range(wl.microbatches):
-            total += 2.0 * T * s.d + 2.0 * T * r + 4.0 * s.d * r * (2 if mb > 0 else 1)
-    return total
+    """Algorithmic bytes of one step's folds (every microbatch but the first
+    accumulates)."""
+    return sum(fold_bytes_per_launch(wl.tokens, s.d, wl.r, mb > 0)
+               for s in wl.matrices for mb in range(wl.microbatches))
+
+
+def apply_bytes_per_matrix(d, k, r, wbytes):
+    """Algorithmic bytes of one matrix's apply: W read and written at its
+    dtype, S read once, v read, v' written (pass 1) and read (pass 2)."""
+    return 2.0 * d * k * wbytes + 4.0 * d * r + 12.0 * d
 
 
 def apply_bytes_per_step(wl):
-    """Algorithmic bytes of one step's apply: W read and written at its
-    dtype, S read once, v read, v' written (pass 1) and read (pass 2)."""
     import torch
     wbytes = 2 if wl.w_dtype == torch.bfloat16 else 4
-    return sum(2.0 * s.d * s.k * wbytes + 4.0 * s.d * wl.r + 12.0 * s.d for s in wl.matrices)
+    return sum(apply_bytes_per_matrix(s.d, s.k, wl.r, wbytes) for s in wl.matrices)
+
+
+def fold_sources_sha256():
+    h = hashlib.sha256()
+    for rel in FOLD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def fold_traffic_record(workload):
+    """The fold's HBM bytes per dispatch from the committed counter summary
+    (profiles/hbm_traffic_<workload>.md, a JSON line after 'traffic-record:'),
+    or None when there is none or it was taken on other fold sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic-record:\s*(\{.*\})", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("fold_sources_sha256") != fold_sources_sha256():
+        return None
+    return rec
 
 
 def parse():
@@ -85,14 +126,13 @@ def parse():
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
-    ap.add_argument("--prepare", action="store_true",
-                    help="one-matrix workloads: build pass 1's Gram matrix ahead, on a side stream "
-                         "during the sketch (logra_sqnorm_prepare), instead of inside pass 1")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time torch.mm (the vendor GEMM) on the fold's contraction and on the "
                          "dense dY^T X it replaces, for context")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--fold-sha", action="store_true",
+                    help="only print the hash of the fold sources (for the counter record)")
     return ap.parse_args()
 
 
@@ -127,7 +167,9 @@ def main():
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
-
+    if args.fold_sha:
+        print(fold_sources_sha256())
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -135,6 +177,7 @@ def main():
     import torch
     from rank_gradient_sketching_sketch_amd import binding as B
     from rank_gradient_sketching_sketch_amd import inputs
+    from rank_gradient_sketching_sketch_amd.step import Matrix, Step
 
     if not os.path.exists(B.LIB_PATH):
         from rank_gradient_sketching_sketch_amd import build_lib
@@ -146,207 +189,97 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     code = B.LOGRA_BF16 if wl.act_dtype == torch.bfloat16 else B.LOGRA_F32
     T, r, nmb = wl.tokens, wl.r, wl.microbatches
+    n_steps = args.warmup + args.steps
 
     # ---- resident state and inputs -------------------------------------
-    mats = []
-    for spec in wl.matrices:
-        mats.append({
-            "spec": spec,
-            "S": torch.empty(spec.d, r, dtype=torch.float32, device=dev),
-            "v": inputs.second_moment(wl, spec, device=dev),
-            "W": inputs.weights(wl, spec, device=dev),
-            "v_new": torch.empty(spec.d, dtype=torch.float32, device=dev),
-            "sq": torch.empty(1, dtype=torch.float32, device=dev),
-        })
-    ws_bytes = max(B.logra_sketch_workspace_bytes(B.MatrixDesc(s.d, s.k, r), T, code)
-                   for s in wl.matrices)
-    sq_ws_bytes = max(B.logra_sqnorm_workspace_bytes(B.MatrixDesc(s.d, s.k, r), code)
-                      for s in wl.matrices)
-    # Independent matrices run on separate streams (matrix i on stream i mod
-    # n), each stream with its own workspaces, so small projections (k, v)
-    # overlap the large ones instead of leaving most of the GPU idle. Four
-    # streams for the sketch phase (HIP gives a process four hardware queues
-    # by default; more streams share them and slowed the apply phase that
-    # follows), three for the apply phase, whose kernels fill the GPU longer.
-    n_sketch = args.streams or min(4, len(mats))
-    n_apply = args.apply_streams or (1 if len(mats) == 1 else 3)
-    n_sketch = max(1, min(n_sketch, len(mats)))
-    n_apply = max(1, min(n_apply, len(mats)))
-    # the projections share the chip with the other sketch streams' work
-    B.logra_set_sketch_concurrency(n_sketch)
-    B.logra_set_apply_concurrency(n_apply)
-    n_streams = max(n_sketch, n_apply)
-    main = torch.cuda.current_stream()
-    lanes = []
-    for i in range(n_streams):
-        lanes.append({
-            "stream": main if i == 0 else torch.cuda.Stream(device=dev),
-            "ws": torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev),
-            "sq_ws": torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev),
-        })
-    for i, m in enumerate(mats):
-        m["lane"] = lanes[i % n_sketch]
-        m["alane"] = lanes[i % n_apply]
-    # Pass 1 in batches: each apply stream's matrices in as few chunks of at
-    # most B.MAX_BATCH as hold them, of equal size (65 matrices: 5 x 13, not
-    # 4 x 16 + 1), one call (two launches) per chunk; a chunk of one matrix
-    # uses the single-matrix call. Each batched matrix's sqnorm is a view of
-    # its chunk's n-float output.
-    batches = []
-    batch_ws_bytes = 0
-    if not args.no_batch:
-        for ln in lanes[:n_apply]:
-            own = [m for m in mats if m["alane"] is ln]
-            n_chunks = -(-len(own) // B.MAX_BATCH)
-            bounds = [len(own) * i // max(1, n_chunks) for i in range(n_chunks + 1)]
-            for c0, c1 in zip(bounds[:-1], bounds[1:]):
-                chunk = own[c0:c1]
-                if len(chunk) == 1:
-                    batches.append((ln, chunk, None, None))
-                    continue
-                sq = torch.empty(len(chunk), dtype=torch.float32, device=dev)
-                for i, m in enumerate(chunk):
-                    m["sq"] = sq[i:i + 1]
-                wsb = B.logra_sqnorm_batch_workspace_bytes(
-                    [B.MatrixDesc(m["spec"].d, m["spec"].k, r) for m in chunk], code)
-                batch_ws_bytes += wsb
-                batches.append((ln, chunk, sq, torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)))
-    # --prepare: a one-matrix workload builds pass 1's Gram matrix (it
-    # depends only on the step's signs) ahead, on a side stream while the
-    # sketch runs, into the workspace pass 1 then reads. Off by default: it
-    # took about 4 us off pass 1 but cost the sketch about 3 %.
-    prep_stream = None
-    if len(mats) == 1 and code == B.LOGRA_BF16 and args.prepare and not args.no_batch:
-        prep_stream = torch.cuda.Stream(device=dev)
+    mats = [Matrix(s.d, s.k, s.matrix_id, W=inputs.weights(wl, s, device=dev),
+                   v=inputs.second_moment(wl, s, device=dev), name="%s.%d" % (s.name, s.layer))
+            for s in wl.matrices]
+    step_runner = Step(mats, r, T, code, device=dev, sketch_lanes=args.streams,
+                       apply_lanes=args.apply_streams, batch_pass1=not args.no_batch)
 
-    # Microbatch buffers: every microbatch has its own; layer stacks rotate
-    # two sets of per-layer inputs (even and odd layers), which keeps a
-    # 28- or 64-layer step within memory while consecutive layers still read
+    # Microbatch buffers. One-matrix workloads: fresh X and dY for every
+    # step and microbatch (as many step sets as the input budget holds,
+    # reused in rotation beyond that). Layer stacks: two sets of per-layer
+    # inputs (even and odd layers) for every microbatch, which keeps a 28-
+    # or 64-layer step within memory while consecutive layers still read
     # different buffers. Projections that read the same activation share X.
-    def xkey(spec, mb):
-        return (spec.layer % 2, inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)
+    per_step_bytes = sum((T * s.k + T * s.d) * (2 if code == B.LOGRA_BF16 else 4)
+                         for s in wl.matrices) * nmb
+    fresh = len(wl.matrices) == 1
+    step_sets = max(1, min(n_steps, INPUT_BUDGET_BYTES // max(1, per_step_bytes))) if fresh else 1
 
-    def ykey(spec, mb):
-        return (spec.layer % 2, spec.name, spec.d, mb)
+    def xkey(spec, step, mb):
+        st = step % step_sets if fresh else 0
+        return (st, spec.layer % 2, inputs.INPUT_GROUP.get(spec.name, spec.name), spec.k, mb)
+
+    def ykey(spec, step, mb):
+        st = step % step_sets if fresh else 0
+        return (st, spec.layer % 2, spec.name, spec.d, mb)
 
     xbuf, ybuf = {}, {}
-    for spec in wl.matrices:
-        for mb in range(nmb):
-            if xkey(spec, mb) not in xbuf:
-                xbuf[xkey(spec, mb)] = inputs.activations(wl, spec, 0, mb, device=dev)
-            if ykey(spec, mb) not in ybuf:
-                ybuf[ykey(spec, mb)] = inputs.output_grads(wl, spec, 0, mb, device=dev)
+    for st in range(step_sets):
+        for spec in wl.matrices:
+            for mb in range(nmb):
+                if xkey(spec, st, mb) not in xbuf:
+                    xbuf[xkey(spec, st, mb)] = inputs.activations(wl, spec, st, mb, device=dev)
+                if ykey(spec, st, mb) not in ybuf:
+                    ybuf[ykey(spec, st, mb)] = inputs.output_grads(wl, spec, st, mb, device=dev)
     torch.cuda.synchronize()
-    stream = main
-
-    def fork():
-        if n_streams > 1:
-            e = torch.cuda.Event()
-            e.record(main)
-            for ln in lanes[1:]:
-                ln["stream"].wait_event(e)
-
-    def join():
-        for ln in lanes[1:]:
-            e = torch.cuda.Event()
-            e.record(ln["stream"])
-            main.wait_event(e)
+    main_stream = torch.cuda.current_stream()
 
     sketch_flop = sketch_flop_per_step(wl)
-    fold_bytes = fold_bytes_per_step(wl)
     apply_bytes = apply_bytes_per_step(wl)
 
-    # Event records cost a few microseconds of GPU time each, so the timed
-    # steps record events only at phase boundaries (sketch | pass 1 | pass 2).
+    # The roofline's kernel: one accumulating fold per timed step (the
+    # largest matrix's, at the middle microbatch), bracketed by an event
+    # pair on the stream it runs on; the phases are bracketed on the main
+    # stream. Event records cost GPU time, so nothing else is bracketed.
+    big = max(range(len(mats)), key=lambda i: mats[i].d * mats[i].k)
+    probe_mb = nmb // 2 if nmb > 1 else 0
+    fold_events, proj_events = [], []
     ev_log = []   # (kind, start_event, end_event)
 
-    def ev():
+    def ev(stream):
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
         return e
 
-    skipped = [0]
+    def sketch_phase(step, timed):
+        def get(i, mb):
+            spec = wl.matrices[i]
+            return xbuf[xkey(spec, step, mb)], ybuf[ykey(spec, step, mb)]
+        marks = step_runner.sketch(step, nmb, get, probe=(big, probe_mb) if timed else None)
+        if marks is not None:
+            proj_events.append(marks[0])
+            fold_events.append(marks[1])
 
-    def sketch_calls(step, m, mb, what):
-        spec = m["spec"]
-        X = xbuf[xkey(spec, mb)]
-        dY = ybuf[ykey(spec, mb)]
-        ln = m["lane"]
-        if what in ("project", "both"):
-            B.logra_sketch_project(m["desc"], X, ln["ws"], ln["stream"])
-        if what in ("fold", "both"):
-            B.logra_sketch_fold(m["desc"], dY, m["S"], mb > 0, ln["ws"], ln["stream"])
+    skipped = [0]
+    ctl_log = []
 
     def one_step(step, timed):
-        for m in mats:
-            spec = m["spec"]
-            m["desc"] = B.MatrixDesc(spec.d, spec.k, r, seed=0, step=step, matrix_id=spec.matrix_id)
-        # microbatch-major, as a backward pass produces them: every matrix's
-        # sketch takes each microbatch in turn
-        e0 = ev() if timed else None
-        fork()
-        if prep_stream is not None:
-            prep_stream.wait_stream(main)
-            B.logra_sqnorm_prepare(mats[0]["desc"], code, mats[0]["alane"]["sq_ws"], prep_stream)
-        for mb in range(nmb):
-            for m in mats:
-                sketch_calls(step, m, mb, "both")
-        join()
-        if prep_stream is not None:
-            main.wait_stream(prep_stream)
-        e1 = ev() if timed else None
-        fork()
-        if batches:
-            for ln, chunk, sq, bws in batches:
-                if sq is None:
-                    m = chunk[0]
-                    if prep_stream is not None:
-                        B.logra_update_sqnorm_prepared(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps,
-                                                       m["v_new"], m["sq"], ln["sq_ws"], None, ln["stream"])
-                    else:
-                        B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
-                                              m["sq"], None, ln["sq_ws"], ln["stream"])
-                else:
-                    B.logra_update_sqnorm_batch([m["desc"] for m in chunk], code, [m["S"] for m in chunk],
-                                                [m["v"] for m in chunk], wl.beta2, wl.eps,
-                                                [m["v_new"] for m in chunk], sq, None, bws, ln["stream"])
-        else:
-            for m in mats:
-                ln = m["alane"]
-                B.logra_update_sqnorm(m["desc"], code, m["S"], m["v"], wl.beta2, wl.eps, m["v_new"],
-                                      m["sq"], None, ln["sq_ws"], ln["stream"])
-        join()
-        e2 = ev() if timed else None
+        e0 = ev(main_stream) if timed else None
+        sketch_phase(step, timed)
+        e1 = ev(main_stream) if timed else None
+        step_runner.pass1(wl.beta2, wl.eps)
+        e2 = ev(main_stream) if timed else None
         # one device->host read of every sqnorm; the library's host controller
         # predicts the step's KL from them (reported, and timed on the host);
         # the update uses the workload's drawn scale, skipping non-finite ones
-        sqs = torch.cat([m["sq"] for m in mats]).cpu().tolist()
+        sqs = step_runner.sqnorms()
         c0 = time.perf_counter()
         gamma, kl_pred, _ = B.logra_kl_step_scale(sqs, wl.lr, KL_PHI, B.logra_kl_budget_at(kl_budget, step))
         ctl_log.append((time.perf_counter() - c0, kl_pred, float(gamma.max()) if len(gamma) else 1.0))
-        # the workload's drawn scales (input generation, kept out of the
-        # timed pass 2); a matrix with a non-finite sqnorm is skipped
-        todo = []
-        for m, sq in zip(mats, sqs):
-            if not math.isfinite(sq):
-                skipped[0] += 1
-                continue
-            todo.append((m, inputs.step_scale(wl, m["spec"], step)))
-        e3 = ev() if timed else None
-        fork()
-        for m, scale in todo:
-            B.logra_rowadam_apply(m["desc"], code, m["S"], m["v_new"], m["W"], wl.lr, scale, wl.eps,
-                                  m["alane"]["stream"])
-            # the update is applied: v' becomes the next step's v (buffer swap)
-            m["v"], m["v_new"] = m["v_new"], m["v"]
-        join()
+        scales = Step.finite_scales(sqs, [inputs.step_scale(wl, s, step) for s in wl.matrices])
+        skipped[0] += sum(1 for s in scales if s is None)
+        e3 = ev(main_stream) if timed else None
+        step_runner.pass2(wl.lr, scales, wl.eps)
         if timed:
-            e4 = ev()
+            e4 = ev(main_stream)
             ev_log.append(("sketch", e0, e1))
             ev_log.append(("sqnorm", e1, e2))
             ev_log.append(("apply", e3, e4))
 
-    ctl_log = []
     for s in range(args.warmup):
         one_step(s, False)
     torch.cuda.synchronize()
@@ -355,26 +288,7 @@ def main():
         one_step(args.warmup + s, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    # Per-kernel averages for the roofline: each half of the sketch launched
-    # back to back over the same microbatch buffers, one event pair around
-    # the run (the average includes the launch gap between kernels).
-    def per_launch_ms(what):
-        reps = max(1, 64 // (nmb * len(mats)))
-        torch.cuda.synchronize()
-        a = ev()
-        fork()
-        for _ in range(reps):
-            for mb in range(nmb):
-                for m in mats:
-                    sketch_calls(0, m, mb, what)
-        join()
-        b = ev()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * nmb * len(mats))
-
-    project_ms = per_launch_ms("project")
-    fold_ms = per_launch_ms("fold")
+    timeouts = step_runner.fold_timeouts()
 
     tot = {"sketch": 0.0, "sqnorm": 0.0, "apply": 0.0}
     for kind, a, b in ev_log:
@@ -384,9 +298,14 @@ def main():
     apply_ms = (tot["sqnorm"] + tot["apply"]) / K
     sketch_tflops = sketch_flop / (sketch_ms * 1e-3) / 1e12
     apply_gbps = apply_bytes / (apply_ms * 1e-3) / 1e9
-    fold_bytes_avg = fold_bytes / (nmb * len(mats))
+    fold_ms = sum(a.elapsed_time(b) for a, b in fold_events) / len(fold_events)
+    proj_ms = sum(a.elapsed_time(b) for a, b in proj_events) / len(proj_events)
+    spec_big = wl.matrices[big]
+    fold_bytes = fold_bytes_per_launch(T, spec_big.d, r, probe_mb > 0)
+    fold_gbps = fold_bytes / (fold_ms * 1e-3) / 1e9
+    rec = fold_traffic_record(wl.name)
+    traffic = None if rec is None else int(round(rec["fold_bytes_per_dispatch"]))
     dev_free, dev_total = torch.cuda.mem_get_info(dev)
-    fold_gbps = fold_bytes_avg / (fold_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -400,14 +319,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if code == B.LOGRA_BF16 else "f32",
-        "data": "synthetic (seeded Gaussian inputs of the workload's shapes; no datasets or weights)",
+        "data": "synthetic (seeded Gaussian inputs of the workload's shapes, generated on the GPU; "
+                "no datasets or weights)",
         "config": {"workload": wl.name, "description": wl.description, "r": r,
                    "microbatches": nmb, "tokens": T, "matrices": len(mats),
-                   "shapes": sorted({(s.d, s.k) for s in wl.matrices})},
+                   "shapes": sorted({(s.d, s.k) for s in wl.matrices}),
+                   "input_sets": ("fresh per step (%d distinct step sets)" % step_sets) if fresh
+                   else "two rotating sets (even / odd layers)"},
         "sketch": {"tflops": round(sketch_tflops, 2),
                    "frac_mfma_peak": round(sketch_tflops / PEAK_BF16_TFLOPS, 4),
                    "ms_per_step": round(sketch_ms, 4),
-                   "project_ms_per_launch": round(project_ms, 5),
+                   "project_ms_per_launch": round(proj_ms, 5),
                    "fold_ms_per_launch": round(fold_ms, 5)},
         "apply": {"GBps": round(apply_gbps, 1), "frac_hbm_peak": round(apply_gbps / PEAK_HBM_GBPS, 4),
                   "ms_per_step": round(apply_ms, 4),
@@ -416,19 +338,24 @@ def main():
         "roofline": {"kernel": "fold_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
                      "achieved": round(fold_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(fold_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": FOLD_TRAFFIC_BYTES.get(wl.name),
-                     "algorithmic_bytes_per_launch": round(fold_bytes_avg)},
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": fold_bytes,
+                     "launch_us": round(fold_ms * 1e3, 2),
+                     "timing": "HIP event pair around one accumulating fold (matrix %s, microbatch %d) of "
+                               "every timed step, on its stream; %d launches" % (mats[big].name, probe_mb,
+                                                                                 len(fold_events)),
+                     "traffic_source": None if rec is None else rec.get("source")},
+        "fold_timeouts": timeouts,
         "state_bytes": {"sketch_plus_v": sum(4 * s.d * r + 4 * s.d for s in wl.matrices),
                         "dense_grad_fp32": sum(4 * s.d * s.k for s in wl.matrices)},
         "memory": {"peak_allocated": torch.cuda.max_memory_allocated(dev),
                    "device_in_use": dev_total - dev_free,
-                   "weights": sum(m["W"].numel() * m["W"].element_size() for m in mats),
+                   "weights": sum(m.W.numel() * m.W.element_size() for m in mats),
                    "microbatch_inputs": sum(t.numel() * t.element_size()
                                             for t in list(xbuf.values()) + list(ybuf.values())),
-                   "workspaces": n_streams * (max(16, ws_bytes) + max(16, sq_ws_bytes)) + batch_ws_bytes},
-        "streams": {"sketch": n_sketch, "apply": n_apply, "sketch_concurrency": n_sketch, "apply_concurrency": n_apply,
-                    "pass1_batches": sum(1 for b in batches if b[2] is not None),
-                    "pass1_prepared": prep_stream is not None},
+                   "workspaces": step_runner.workspace_bytes},
+        "streams": {"sketch": step_runner.n_sketch, "apply": step_runner.n_apply,
+                    "pass1_batches": sum(1 for b in step_runner.batches if b[2] is not None)},
         "controller": {"fisher_scale": KL_PHI,
                        "budget": [kl_budget.delta_start, kl_budget.delta_end, kl_budget.anneal_steps],
                        "kl_pred_last_step": ctl_log[-1][1], "gamma_last_step": ctl_log[-1][2],
@@ -439,8 +366,13 @@ def main():
     if args.yardstick:
         result["yardstick"] = yardstick(wl, fold_ms if len(mats) == 1 else None)
     if not args.no_cpu_baseline:
+        del xbuf, ybuf
+        torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
+    if timeouts:
+        print("fold time-outs: %d workgroups gave up waiting for their partner" % timeouts, file=sys.stderr)
+        sys.exit(3)
 
 
 def yardstick(wl, fold_ms):
@@ -488,9 +420,13 @@ def yardstick(wl, fold_ms):
 
 
 def cpu_baseline(wl, budget_s=15.0):
-    """The oracle as it stands, timed on the host: the step's sketch-accumulate
-    units (P = X A^T, then S += dY^T P over all rows, fp64) in the order the
-    GPU step takes them, until about budget_s seconds have been spent."""
+    """The oracle as it stands, timed on the host (input generation and
+    conversion excluded): (a) the step's sketch-accumulate units (P = X A^T,
+    then S += dY^T P over all rows, fp64) in the order the GPU step takes
+    them, until about budget_s seconds have been spent; (b) one whole apply
+    (rowsq, v', the sqnorm term and W') over every row of the largest
+    matrix, from the sketch (a) left; (c) one sketch unit on one thread."""
+    import numpy as np
     import oracle
     from rank_gradient_sketching_sketch_amd import inputs
     done, flop, spent = 0, 0.0, 0.0
@@ -513,12 +449,27 @@ def cpu_baseline(wl, budget_s=15.0):
            "kind": "oracle", "seconds": round(spent, 2), "cpu": cpu_model(),
            "sample": "%d of the step's %d sketch-accumulate units (microbatch x matrix, %d tokens each), "
                      "all rows, fp64" % (done, total, wl.tokens)}
-    # the same oracle on one thread, for one unit (the first microbatch of the
-    # largest matrix)
+    # (b) the apply of the largest matrix, every row
     spec = max(wl.matrices, key=lambda s: s.d * s.k)
+    A = oracle.sign_matrix(0, 0, spec.matrix_id, wl.r, spec.k)
+    S_big = S.get(spec.matrix_id)
+    if S_big is None:
+        S_big = np.zeros((spec.d, wl.r))
+    v = inputs.second_moment(wl, spec).double().numpy()
+    W = inputs.weights(wl, spec).double().numpy()
+    t0 = time.perf_counter()
+    oracle.rowadam_rows(S_big, A, v, W, beta2=wl.beta2, eps=wl.eps, lr=wl.lr,
+                        scale=inputs.step_scale(wl, spec, 0))
+    t_apply = time.perf_counter() - t0
+    wbytes = 2 if wl.w_dtype.itemsize == 2 else 4
+    out["apply"] = {"value": round(apply_bytes_per_matrix(spec.d, spec.k, wl.r, wbytes) / t_apply / 1e9, 4),
+                    "unit": "GB/s", "seconds": round(t_apply, 2), "cores": oracle.num_threads(),
+                    "sample": "one apply (passes 1 and 2, literal S A) of %d x %d, all %d rows, fp64; GB/s by "
+                              "the GPU apply's algorithmic bytes" % (spec.d, spec.k, spec.d)}
+    # (c) the same oracle on one thread, for one unit (the first microbatch of
+    # the largest matrix)
     X = inputs.activations(wl, spec, 0, 0).double().numpy()
     dY = inputs.output_grads(wl, spec, 0, 0).double().numpy()
-    A = oracle.sign_matrix(0, 0, spec.matrix_id, wl.r, spec.k)
     threads = oracle.num_threads()
     oracle.set_num_threads(1)
     try:

@@ -40,11 +40,11 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller (except the
  *     host arrays of the step controller at the end). The library
- *     allocates nothing and is reentrant; its only mutable global state
- *     is three process-wide settings read when a kernel is launched: the
- *     fold's partner-wait limit (logra_set_fold_wait_limit) and the sketch
- *     and apply concurrency hints (logra_set_sketch_concurrency,
- *     logra_set_apply_concurrency).
+ *     allocates nothing and keeps no mutable global state: everything a
+ *     launch depends on is in its arguments (scheduling hints and the
+ *     fold's wait limit included, in a caller-owned logra_launch_opts), so
+ *     the calls are reentrant and may be made from several host threads at
+ *     once, on the same or different streams.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued asynchronously on it; results are visible after the caller
  *     synchronises the stream.
@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LOGRA_ABI_VERSION 2
+#define LOGRA_ABI_VERSION 3
 
 typedef enum logra_status {
     LOGRA_OK = 0,
@@ -93,6 +93,50 @@ typedef struct logra_matrix {
     uint64_t step;
     uint64_t matrix_id;
 } logra_matrix;
+
+/*
+ * Per-call launch options (host struct, owned by the caller, read during the
+ * call only). Pass NULL for the defaults; a zeroed struct means the same.
+ * None of these is an operation of the pages: they steer how this
+ * implementation shares the chip and guard its in-kernel exchange.
+ *   sketch_concurrency  independent sketch calls (of different matrices)
+ *                       the caller keeps in flight at once on separate
+ *                       streams, this one included; 0 or 1 = this call runs
+ *                       alone. With n > 1 the projection sizes its
+ *                       workgroups for a 1/n share of the chip (fewer,
+ *                       taller ones, 64 tokens each, never fewer than 128 of
+ *                       them): faster when other streams fill the rest of
+ *                       the chip, slower when the call has it to itself.
+ *                       Results stay within the same tolerance of the
+ *                       oracle (the projection's summation order differs
+ *                       between the two shapes). Range [0, 256].
+ *   apply_concurrency   the same for pass 2 (logra_rowadam_apply): with
+ *                       n > 1, the bf16 pass 2 of a large matrix (at least
+ *                       1024 tiles of 256 rows x 64 columns) deals its work
+ *                       over 128 workgroups instead of 256. Range [0, 256].
+ *   fold_wait_limit     polls a fold workgroup makes for the workgroup it
+ *                       exchanges partial sums with (bf16 path, tall tiles
+ *                       split over two token halves); 0 = the default of
+ *                       2^20 (about a second). A workgroup that gives up
+ *                       writes its rows of S as NaN instead of waiting
+ *                       longer, and counts itself in fold_timeouts. A
+ *                       negative value makes every such workgroup give up
+ *                       without polling, which forces that path from the
+ *                       host (for tests of it).
+ *   reserved            must be 0 (INVALID_ARGUMENT otherwise).
+ *   fold_timeouts       DEVICE pointer to one int32, or NULL. Every fold
+ *                       workgroup that gives up adds 1 to it (a device-scope
+ *                       atomic add), so a caller can tell a time-out from
+ *                       non-finite inputs. The caller zeroes it and reads
+ *                       it when it likes; one counter may serve many calls.
+ */
+typedef struct logra_launch_opts {
+    int32_t sketch_concurrency;
+    int32_t apply_concurrency;
+    int32_t fold_wait_limit;
+    int32_t reserved;
+    int32_t *fold_timeouts;
+} logra_launch_opts;
 
 /* ABI version of the loaded library (LOGRA_ABI_VERSION). */
 int logra_abi_version(void);
@@ -143,18 +187,22 @@ size_t logra_sketch_workspace_bytes(const logra_matrix *m, int64_t T, int act_dt
  *   dY       T x d, row stride lddy >= d.
  *   S        d x r fp32, row-major, stride r; in/out.
  *   ws       device workspace of ws_bytes >= logra_sketch_workspace_bytes().
+ *   opts     launch options (see logra_launch_opts), or NULL.
  * Requirements of the bf16 path: r in {32, 64, 128, 256}; d, k, ldx, lddy
- *   multiples of 8; X, dY 16-byte aligned. The fp32 path takes any r in
+ *   multiples of 8; X, dY 16-byte aligned; each of X, dY, the projection
+ *   (about T x r bf16) and 64 d x r bytes below 2^31 bytes (the kernels
+ *   address them with 32-bit offsets). The fp32 path takes any r in
  *   [1, 1024] and any d, k >= 1. S and ws must be 16-byte aligned.
  * Errors: INVALID_ARGUMENT (null pointer when T > 0, sizes <= 0, T < 0,
- *   ld < cols, misalignment), UNSUPPORTED (r or shape outside the above,
- *   unknown dtype), WORKSPACE (ws NULL or ws_bytes too small), HIP.
+ *   ld < cols, misalignment, bad opts), UNSUPPORTED (r or shape outside the
+ *   above, unknown dtype), WORKSPACE (ws NULL or ws_bytes too small), HIP.
  */
 logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_dtype,
                                      const void *X, int64_t ldx,
                                      const void *dY, int64_t lddy,
                                      float *S, int accumulate,
-                                     void *ws, size_t ws_bytes, void *stream);
+                                     void *ws, size_t ws_bytes,
+                                     const logra_launch_opts *opts, void *stream);
 
 /*
  * logra_sketch_project / logra_sketch_fold -- the two halves of
@@ -174,60 +222,13 @@ logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_d
  */
 logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtype,
                                   const void *X, int64_t ldx,
-                                  void *ws, size_t ws_bytes, void *stream);
+                                  void *ws, size_t ws_bytes,
+                                  const logra_launch_opts *opts, void *stream);
 logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
                                const void *dY, int64_t lddy,
                                float *S, int accumulate,
-                               void *ws, size_t ws_bytes, void *stream);
-
-/*
- * logra_set_fold_wait_limit -- how long a fold workgroup waits for its
- * partner. On the bf16 path, tall tiles are split over two token halves
- * whose workgroups exchange partial sums inside the kernel; each polls the
- * other's flag at most `polls` times (default 1 << 20, about a second) and,
- * if the partner has not arrived, writes its rows of S as NaN instead of
- * waiting longer. A negative value makes them give up without polling,
- * which forces that path from the host (for tests of it). The setting is
- * process-wide and applies to folds launched after the call; it is not
- * synchronised with launches made at the same time from other threads.
- * previous: host, may be NULL; receives the limit in force before the call.
- * Not an operation of the pages: a guard of this implementation's exchange.
- * Errors: none.
- */
-logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous);
-
-/*
- * logra_set_sketch_concurrency -- how many independent sketch calls
- * (logra_sketch_accumulate / logra_sketch_project of different matrices)
- * the caller keeps in flight at once on separate streams; default 1. The
- * projection sizes its workgroups for a 1/n share of the chip: with a larger
- * n it uses fewer, taller workgroups (64 tokens each, never fewer than 128
- * of them) that expand each sign fragment for more tokens, which is faster
- * when other streams fill the rest of the chip and slower when the call has
- * it to itself. Results stay
- * within the same tolerance of the oracle (the summation order of the
- * projection differs between the two shapes). Process-wide; applies to
- * projections launched after the call.
- * previous: host, may be NULL; receives the value in force before the call.
- * Not an operation of the pages: a scheduling hint of this implementation.
- * Errors: INVALID_ARGUMENT for n < 1 or n > 256 (nothing changes).
- */
-logra_status logra_set_sketch_concurrency(int32_t n, int32_t *previous);
-
-/*
- * logra_set_apply_concurrency -- how many apply calls (logra_rowadam_apply
- * of different matrices) the caller keeps in flight at once on separate
- * streams; default 1. With n > 1 the bf16 pass 2 of a large matrix (at
- * least 1024 tiles of 256 rows x 64 columns) deals its work over 128
- * workgroups instead of 256 (each walks a longer range of W), which is
- * faster when other streams fill the rest of the chip and slower when the
- * call has it to itself. Results stay within the same tolerance of the
- * oracle. Process-wide; applies to launches after the call.
- * previous: host, may be NULL; receives the value in force before the call.
- * Not an operation of the pages: a scheduling hint of this implementation.
- * Errors: INVALID_ARGUMENT for n < 1 or n > 256 (nothing changes).
- */
-logra_status logra_set_apply_concurrency(int32_t n, int32_t *previous);
+                               void *ws, size_t ws_bytes,
+                               const logra_launch_opts *opts, void *stream);
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs
@@ -341,16 +342,18 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
  *   S        d x r fp32. v_new: d fp32, in.
  *   W        d x k, row stride ldw >= k, dtype w_dtype (fp32 math, stored
  *            back at its dtype; bf16 by round-to-nearest-even), in/out.
+ *   opts     launch options (apply_concurrency is the one read here), or NULL.
  * Requirements: as logra_update_sqnorm; bf16 W or bf16 compute also need
- *   ldw multiple of 8 and W 16-byte aligned.
- * Errors: INVALID_ARGUMENT (nulls, eps < 0, ld, misalignment), UNSUPPORTED,
- *   HIP.
+ *   ldw multiple of 8, W 16-byte aligned and d x ldw elements of W below
+ *   2^31 bytes.
+ * Errors: INVALID_ARGUMENT (nulls, eps < 0, ld, misalignment, bad opts),
+ *   UNSUPPORTED, HIP.
  */
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype,
                                  const float *S, const float *v_new,
                                  void *W, int w_dtype, int64_t ldw,
                                  float lr, float scale, float eps,
-                                 void *stream);
+                                 const logra_launch_opts *opts, void *stream);
 
 /*
  * Predicted-KL step control (host side; no device work).

@@ -10,8 +10,7 @@ from __future__ import annotations
 __all__ = [
     "logra_abi_version", "logra_status_string", "logra_sign_words",
     "logra_sketch_workspace_bytes", "logra_sketch_accumulate",
-    "logra_sketch_project", "logra_sketch_fold", "logra_set_fold_wait_limit",
-    "logra_set_sketch_concurrency", "logra_set_apply_concurrency",
+    "logra_sketch_project", "logra_sketch_fold", "LaunchOpts",
     "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
     "logra_sqnorm_prepare", "logra_update_sqnorm_prepared",
     "logra_sqnorm_batch_workspace_bytes", "logra_update_sqnorm_batch",

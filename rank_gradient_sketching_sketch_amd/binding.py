@@ -39,6 +39,28 @@ class MatrixDesc(ctypes.Structure):
         super().__init__(int(d), int(k), int(r), int(seed), int(step), int(matrix_id))
 
 
+class LaunchOpts(ctypes.Structure):
+    """logra_launch_opts: per-call scheduling hints and the fold's wait
+    guard (0 = default for each field). fold_timeouts may be given as an
+    int32 device tensor of one element (or a raw device address); every fold
+    workgroup that gives up on its partner adds 1 to it."""
+    _fields_ = [("sketch_concurrency", ctypes.c_int32), ("apply_concurrency", ctypes.c_int32),
+                ("fold_wait_limit", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("fold_timeouts", ctypes.c_void_p)]
+
+    def __init__(self, sketch_concurrency=0, apply_concurrency=0, fold_wait_limit=0,
+                 fold_timeouts=None):
+        addr = None
+        if fold_timeouts is not None:
+            if isinstance(fold_timeouts, torch.Tensor):
+                if fold_timeouts.dtype != torch.int32 or fold_timeouts.numel() < 1:
+                    raise LograError(1, "fold_timeouts: one-element int32 device tensor expected")
+                addr = fold_timeouts.data_ptr()
+            else:
+                addr = int(fold_timeouts)
+        super().__init__(int(sketch_concurrency), int(apply_concurrency), int(fold_wait_limit), 0, addr)
+
+
 class KLBudget(ctypes.Structure):
     """logra_kl_budget: KL budget annealed linearly from delta_start to
     delta_end over anneal_steps steps."""
@@ -66,6 +88,7 @@ def load_library():
     P, i64, u64, f32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                  ctypes.c_float, ctypes.c_int, ctypes.c_size_t)
     D = ctypes.POINTER(MatrixDesc)
+    O = ctypes.POINTER(LaunchOpts)
     lib.logra_abi_version.restype = i32
     lib.logra_abi_version.argtypes = []
     lib.logra_status_string.restype = ctypes.c_char_p
@@ -75,17 +98,11 @@ def load_library():
     lib.logra_sketch_workspace_bytes.restype = sz
     lib.logra_sketch_workspace_bytes.argtypes = [D, i64, i32]
     lib.logra_sketch_accumulate.restype = i32
-    lib.logra_sketch_accumulate.argtypes = [D, i64, i32, P, i64, P, i64, P, i32, P, sz, P]
+    lib.logra_sketch_accumulate.argtypes = [D, i64, i32, P, i64, P, i64, P, i32, P, sz, O, P]
     lib.logra_sketch_project.restype = i32
-    lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, P]
+    lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, O, P]
     lib.logra_sketch_fold.restype = i32
-    lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, P]
-    lib.logra_set_fold_wait_limit.restype = i32
-    lib.logra_set_fold_wait_limit.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
-    lib.logra_set_sketch_concurrency.restype = i32
-    lib.logra_set_sketch_concurrency.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
-    lib.logra_set_apply_concurrency.restype = i32
-    lib.logra_set_apply_concurrency.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, O, P]
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
@@ -95,7 +112,7 @@ def load_library():
     lib.logra_sqnorm_prepare.restype = i32
     lib.logra_sqnorm_prepare.argtypes = [D, i32, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
-    lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, i32, i64, f32, f32, f32, P]
+    lib.logra_rowadam_apply.argtypes = [D, i32, P, P, P, i32, i64, f32, f32, f32, O, P]
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.logra_sqnorm_batch_workspace_bytes.restype = sz
     lib.logra_sqnorm_batch_workspace_bytes.argtypes = [i32, D, i32]
@@ -133,6 +150,10 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+def _opts(opts):
+    return None if opts is None else ctypes.byref(opts)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -160,14 +181,15 @@ def logra_sketch_workspace_bytes(m: MatrixDesc, T: int, act_dtype: int) -> int:
 
 def logra_sketch_accumulate(m: MatrixDesc, X: torch.Tensor, dY: torch.Tensor, S: torch.Tensor,
                             accumulate: bool, ws: Optional[torch.Tensor] = None,
-                            stream=None) -> None:
+                            stream=None, opts: Optional[LaunchOpts] = None) -> None:
     """S (+)= dY^T (X A^T) for one microbatch; X is T x k, dY is T x d."""
     T = X.shape[0]
     code = _dtype_code(X)
     ws, ws_bytes = _sketch_ws(m, T, code, S.device, ws)
     _check(load_library().logra_sketch_accumulate(
         ctypes.byref(m), T, code, _ptr(X), _ld(X), _ptr(dY), _ld(dY), _ptr(S),
-        1 if accumulate else 0, _ptr(ws), ws_bytes, _stream(stream)), "logra_sketch_accumulate")
+        1 if accumulate else 0, _ptr(ws), ws_bytes, _opts(opts), _stream(stream)),
+        "logra_sketch_accumulate")
 
 
 def _sketch_ws(m, T, code, device, ws):
@@ -177,51 +199,22 @@ def _sketch_ws(m, T, code, device, ws):
     return ws, ws.numel() * ws.element_size()
 
 
-def logra_set_fold_wait_limit(polls: int) -> int:
-    """Polls a fold member makes for its partner before writing its rows as
-    NaN (negative: give up at once, to force that path); returns the previous
-    limit. Process-wide."""
-    prev = ctypes.c_int32(0)
-    _check(load_library().logra_set_fold_wait_limit(int(polls), ctypes.byref(prev)),
-           "logra_set_fold_wait_limit")
-    return int(prev.value)
-
-
-def logra_set_sketch_concurrency(n: int) -> int:
-    """Independent sketch calls kept in flight on separate streams (the
-    projection sizes its workgroups for that share of the chip); returns the
-    previous value. Process-wide."""
-    prev = ctypes.c_int32(0)
-    _check(load_library().logra_set_sketch_concurrency(int(n), ctypes.byref(prev)),
-           "logra_set_sketch_concurrency")
-    return int(prev.value)
-
-
-def logra_set_apply_concurrency(n: int) -> int:
-    """Independent apply calls kept in flight on separate streams (pass 2
-    sizes its grid for that share of the chip); returns the previous value.
-    Process-wide."""
-    prev = ctypes.c_int32(0)
-    _check(load_library().logra_set_apply_concurrency(int(n), ctypes.byref(prev)),
-           "logra_set_apply_concurrency")
-    return int(prev.value)
-
-
-def logra_sketch_project(m: MatrixDesc, X: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+def logra_sketch_project(m: MatrixDesc, X: torch.Tensor, ws: torch.Tensor, stream=None,
+                         opts: Optional[LaunchOpts] = None) -> None:
     """workspace <- X A^T for one microbatch (first half of sketch_accumulate)."""
     ws, nb = _sketch_ws(m, X.shape[0], _dtype_code(X), X.device, ws)
     _check(load_library().logra_sketch_project(
         ctypes.byref(m), X.shape[0], _dtype_code(X), _ptr(X), _ld(X), _ptr(ws), nb,
-        _stream(stream)), "logra_sketch_project")
+        _opts(opts), _stream(stream)), "logra_sketch_project")
 
 
 def logra_sketch_fold(m: MatrixDesc, dY: torch.Tensor, S: torch.Tensor, accumulate: bool,
-                      ws: torch.Tensor, stream=None) -> None:
+                      ws: torch.Tensor, stream=None, opts: Optional[LaunchOpts] = None) -> None:
     """S (+)= dY^T (X A^T) with the projection left in ws by logra_sketch_project."""
     ws, nb = _sketch_ws(m, dY.shape[0], _dtype_code(dY), dY.device, ws)
     _check(load_library().logra_sketch_fold(
         ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(S),
-        1 if accumulate else 0, _ptr(ws), nb, _stream(stream)), "logra_sketch_fold")
+        1 if accumulate else 0, _ptr(ws), nb, _opts(opts), _stream(stream)), "logra_sketch_fold")
 
 
 def logra_sqnorm_workspace_bytes(m: MatrixDesc, compute_dtype: int) -> int:
@@ -263,12 +256,13 @@ def logra_update_sqnorm_prepared(m: MatrixDesc, compute_dtype: int, S: torch.Ten
 
 
 def logra_rowadam_apply(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v_new: torch.Tensor,
-                        W: torch.Tensor, lr: float, scale: float, eps: float, stream=None) -> None:
+                        W: torch.Tensor, lr: float, scale: float, eps: float, stream=None,
+                        opts: Optional[LaunchOpts] = None) -> None:
     """Pass 2: W -= lr * scale * (S A) / (sqrt(v_new) + eps), row-wise; writes W only."""
     _check(load_library().logra_rowadam_apply(
         ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v_new), _ptr(W),
         _dtype_code(W), _ld(W), float(lr), float(scale), float(eps),
-        _stream(stream)), "logra_rowadam_apply")
+        _opts(opts), _stream(stream)), "logra_rowadam_apply")
 
 
 def logra_kl_budget_at(budget: KLBudget, step: int) -> float:

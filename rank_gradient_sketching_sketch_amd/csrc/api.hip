@@ -41,6 +41,28 @@ size_t sqnorm_ws_bytes(const logra_matrix *m, int compute_dtype) {
 // Buffer views address at most 2^31 bytes.
 bool fits_view(int64_t rows, int64_t ld, int64_t elem) { return rows * ld * elem < (1ll << 31); }
 
+// Launch options with their defaults filled in (NULL = all defaults).
+struct Opts {
+    int sketch_concurrency = 1;
+    int apply_concurrency = 1;
+    FoldWait wait;
+};
+
+bool read_opts(const logra_launch_opts *o, Opts *out) {
+    Opts r;
+    if (o) {
+        if (o->reserved != 0) return false;
+        if (o->sketch_concurrency < 0 || o->sketch_concurrency > 256) return false;
+        if (o->apply_concurrency < 0 || o->apply_concurrency > 256) return false;
+        if (o->sketch_concurrency > 0) r.sketch_concurrency = o->sketch_concurrency;
+        if (o->apply_concurrency > 0) r.apply_concurrency = o->apply_concurrency;
+        if (o->fold_wait_limit != 0) r.wait.spin_limit = o->fold_wait_limit;
+        r.wait.timeouts = o->fold_timeouts;
+    }
+    *out = r;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,26 +78,6 @@ const char *logra_status_string(int status) {
     case LOGRA_ERR_HIP: return "LOGRA_ERR_HIP";
     default: return "LOGRA_UNKNOWN_STATUS";
     }
-}
-
-logra_status logra_set_fold_wait_limit(int32_t polls, int32_t *previous) {
-    const int prev = logra::set_fold_spin_limit(polls);
-    if (previous) *previous = prev;
-    return LOGRA_OK;
-}
-
-logra_status logra_set_sketch_concurrency(int32_t n, int32_t *previous) {
-    if (n < 1 || n > 256) return LOGRA_ERR_INVALID_ARGUMENT;
-    const int prev = logra::set_sketch_concurrency(n);
-    if (previous) *previous = prev;
-    return LOGRA_OK;
-}
-
-logra_status logra_set_apply_concurrency(int32_t n, int32_t *previous) {
-    if (n < 1 || n > 256) return LOGRA_ERR_INVALID_ARGUMENT;
-    const int prev = logra::set_apply_concurrency(n);
-    if (previous) *previous = prev;
-    return LOGRA_OK;
 }
 
 logra_status logra_sign_words(const logra_matrix *m, uint64_t *words, void *stream) {
@@ -105,6 +107,9 @@ static logra_status check_sketch(const logra_matrix *m, int64_t T, int act_dtype
     if (T > (1ll << 30)) return LOGRA_ERR_UNSUPPORTED;
     if (act_dtype == LOGRA_BF16) {
         if (!bf16_rank_ok(m->r) || m->d % 8 || m->k % 8) return LOGRA_ERR_UNSUPPORTED;
+        // the projection (ceil(T/32) blocks of 32 tokens x r, bf16) is read
+        // through a 32-bit buffer view
+        if (!fits_view(T + 32, m->r, 2)) return LOGRA_ERR_UNSUPPORTED;
     } else if (m->r > 1024) {
         return LOGRA_ERR_UNSUPPORTED;
     }
@@ -136,57 +141,65 @@ static logra_status check_fold(const logra_matrix *m, int64_t T, int act_dtype, 
 }
 
 static hipError_t do_project(const logra_matrix *m, int64_t T, int act_dtype, const void *X,
-                             int64_t ldx, void *ws, hipStream_t st) {
+                             int64_t ldx, void *ws, const Opts &o, hipStream_t st) {
     if (T == 0) return hipSuccess;
     const uint64_t key = stream_key(m->seed, m->step, m->matrix_id);
     const float c = inv_sqrt_rank(m->r);
     const int r = static_cast<int>(m->r);
     if (act_dtype == LOGRA_BF16)
-        return launch_project_bf16(r, T, m->d, m->k, key, c, static_cast<const uint16_t *>(X), ldx, ws, st);
+        return launch_project_bf16(r, T, m->d, m->k, key, c, static_cast<const uint16_t *>(X), ldx, ws,
+                                   o.sketch_concurrency, st);
     return launch_project_f32(r, T, m->k, key, c, static_cast<const float *>(X), ldx, ws, st);
 }
 
 static hipError_t do_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
-                          int64_t lddy, float *S, int accumulate, void *ws, hipStream_t st) {
+                          int64_t lddy, float *S, int accumulate, void *ws, const Opts &o, hipStream_t st) {
     if (T == 0) return accumulate ? hipSuccess : launch_fill_zero(S, m->d * m->r, st);
     const int r = static_cast<int>(m->r);
     if (act_dtype == LOGRA_BF16)
         return launch_fold_bf16(r, T, m->d, m->k, static_cast<const uint16_t *>(dY), lddy, S,
-                                accumulate ? 1 : 0, ws, st);
+                                accumulate ? 1 : 0, ws, o.wait, st);
     return launch_fold_f32(r, T, m->d, static_cast<const float *>(dY), lddy, S, accumulate ? 1 : 0,
                            ws, st);
 }
 
 logra_status logra_sketch_project(const logra_matrix *m, int64_t T, int act_dtype, const void *X,
-                                  int64_t ldx, void *ws, size_t ws_bytes, void *stream) {
+                                  int64_t ldx, void *ws, size_t ws_bytes, const logra_launch_opts *opts,
+                                  void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
     logra_status e = check_sketch(m, T, act_dtype);
     if (e == LOGRA_OK) e = check_project(m, T, act_dtype, X, ldx, ws, ws_bytes);
     if (e != LOGRA_OK) return e;
-    return from_hip(do_project(m, T, act_dtype, X, ldx, ws, static_cast<hipStream_t>(stream)));
+    return from_hip(do_project(m, T, act_dtype, X, ldx, ws, o, static_cast<hipStream_t>(stream)));
 }
 
 logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
                                int64_t lddy, float *S, int accumulate, void *ws,
-                               size_t ws_bytes, void *stream) {
+                               size_t ws_bytes, const logra_launch_opts *opts, void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
     logra_status e = check_sketch(m, T, act_dtype);
     if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
     if (e != LOGRA_OK) return e;
-    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws,
+    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, o,
                             static_cast<hipStream_t>(stream)));
 }
 
 logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_dtype,
                                      const void *X, int64_t ldx, const void *dY, int64_t lddy,
                                      float *S, int accumulate, void *ws, size_t ws_bytes,
-                                     void *stream) {
+                                     const logra_launch_opts *opts, void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
     logra_status e = check_sketch(m, T, act_dtype);
     if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
     if (e == LOGRA_OK) e = check_project(m, T, act_dtype, X, ldx, ws, ws_bytes);
     if (e != LOGRA_OK) return e;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t h = do_project(m, T, act_dtype, X, ldx, ws, st);
+    hipError_t h = do_project(m, T, act_dtype, X, ldx, ws, o, st);
     if (h != hipSuccess) return LOGRA_ERR_HIP;
-    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, st));
+    return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, o, st));
 }
 
 size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype) {
@@ -345,7 +358,7 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
         it.v = v[i];
         it.v_new = v_new[i];
         it.rowsq = rowsq ? rowsq[i] : nullptr;
-        it.partials = reinterpret_cast<float *>(base);
+        it.slots = reinterpret_cast<uint64_t *>(base);
         it.M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
         it.counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
         it.key = stream_key(ms[i].seed, ms[i].step, ms[i].matrix_id);
@@ -363,7 +376,10 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
 
 logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const float *S,
                                  const float *v_new, void *W, int w_dtype, int64_t ldw,
-                                 float lr, float scale, float eps, void *stream) {
+                                 float lr, float scale, float eps, const logra_launch_opts *opts,
+                                 void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
     logra_status stt = check_apply_common(m, compute_dtype, S, 0.f, eps);
     if (stt != LOGRA_OK) return stt;
     if (!v_new || !W) return LOGRA_ERR_INVALID_ARGUMENT;
@@ -379,7 +395,7 @@ logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const
     a.W = W;
     a.w_bf16 = w_dtype == LOGRA_BF16 ? 1 : 0;
     a.ldw = ldw;
-    return from_hip(compute_dtype == LOGRA_BF16 ? launch_rowadam_bf16(a, st)
+    return from_hip(compute_dtype == LOGRA_BF16 ? launch_rowadam_bf16(a, o.apply_concurrency, st)
                                                 : launch_apply_f32(1, a, st));
 }
 

@@ -47,23 +47,16 @@ constexpr int kApplyWaves = 8;
 constexpr int kApplyCols = 64;         // columns per column tile (one sign word)
 constexpr int kApplyWGs = 256;         // workgroups (one per compute unit)
 
-// Apply calls the caller keeps in flight at once on separate streams
-// (process-wide; logra_set_apply_concurrency). With more than one, pass 2
-// of a large matrix (at least kConcurrentMinUnits 256-row units) deals its
-// units over half as many workgroups, which then walk longer ranges while
-// the other streams fill the rest of the chip; smaller matrices measured
-// slower that way and keep the full grid.
+// With more than one apply call in flight at once on separate streams (the
+// caller's apply_concurrency launch option), pass 2 of a large matrix (at
+// least kConcurrentMinUnits 256-row units) deals its units over half as
+// many workgroups, which then walk longer ranges while the other streams
+// fill the rest of the chip; smaller matrices measured slower that way and
+// keep the full grid.
 constexpr int64_t kConcurrentMinUnits = 1024;
-static int g_apply_concurrency = 1;
 
-int set_apply_concurrency(int n) {
-    const int prev = g_apply_concurrency;
-    g_apply_concurrency = n;
-    return prev;
-}
-
-static int apply_wgs(int64_t units256) {
-    return g_apply_concurrency > 1 && units256 >= kConcurrentMinUnits ? kApplyWGs / 2 : kApplyWGs;
+static int apply_wgs(int64_t units256, int concurrency) {
+    return concurrency > 1 && units256 >= kConcurrentMinUnits ? kApplyWGs / 2 : kApplyWGs;
 }
 constexpr int kTallTileUnitsPerWG = 4;  // 256-row units per workgroup from which 256-row tiles are used
 constexpr int kStagePitch = 144;       // bytes per staged row of a wave's updated bf16 block
@@ -359,7 +352,7 @@ __global__ __launch_bounds__(512) void rowadam_bf16_kernel(ApplyArgs a, int n_ct
             }
         }
     }
-    // the last unit's update: slot (u_end - 1 - u_begin) % 3
+    // the last unit's update: slot (u_end - 1 - u_begin) % 2
     if ((u_end - 1 - u_begin) % 2 == 0)
         finish(prev, cf_prev, pp, wb[0]);
     else
@@ -386,19 +379,19 @@ static hipError_t rowadam_rb(const ApplyArgs &a, int wgs, hipStream_t st) {
 // amortise loading its rows of S (256 KB at r = 256), otherwise 128 rows,
 // which halve that load at the price of sign fragments shared by fewer rows.
 template <int R>
-static hipError_t rowadam_r(const ApplyArgs &a, hipStream_t st) {
+static hipError_t rowadam_r(const ApplyArgs &a, int concurrency, hipStream_t st) {
     const int64_t units256 = ((a.D + kApplyRowsMax - 1) / kApplyRowsMax) * ((a.K + kApplyCols - 1) / kApplyCols);
-    const int wgs = apply_wgs(units256);
+    const int wgs = apply_wgs(units256, concurrency);
     if (units256 >= static_cast<int64_t>(kTallTileUnitsPerWG) * wgs) return rowadam_rb<R, 2>(a, wgs, st);
     return rowadam_rb<R, 1>(a, wgs, st);
 }
 
-hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st) {
+hipError_t launch_rowadam_bf16(const ApplyArgs &a, int concurrency, hipStream_t st) {
     switch (a.R) {
-    case 32: return rowadam_r<32>(a, st);
-    case 64: return rowadam_r<64>(a, st);
-    case 128: return rowadam_r<128>(a, st);
-    case 256: return rowadam_r<256>(a, st);
+    case 32: return rowadam_r<32>(a, concurrency, st);
+    case 64: return rowadam_r<64>(a, concurrency, st);
+    case 128: return rowadam_r<128>(a, concurrency, st);
+    case 256: return rowadam_r<256>(a, concurrency, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -33,20 +33,29 @@
 //     buffer as raw MFMA fragments (1 KB per wave and block, device-coherent
 //     stores), raises its flag, waits for the other's flag, and forms
 //     S = [S +] (part_0 + part_1) for its rows; fp32 addition commutes, so the
-//     result does not depend on which member finishes first. Members take
-//     tickets from a counter when they start and a tile's two members hold
-//     consecutive tickets, so a member only ever waits for a workgroup that has
-//     already started: no co-residency beyond two workgroups is assumed.
+//     result does not depend on which member finishes first. The flag is
+//     raised with an agent-scope release (after a workgroup barrier, so it
+//     covers every thread's fragment stores) and read with an agent-scope
+//     acquire, which orders the fragments before it on any XCD.
+//     Members take tickets from a counter when they start and a tile's two
+//     members hold consecutive tickets (2i, 2i + 1). Tickets are drawn in
+//     start order, so the workgroups that have started hold a prefix of the
+//     tickets and at most one started member (the holder of the last, even
+//     ticket) waits for a workgroup that has not started yet; that one starts
+//     as soon as any slot on the chip frees up, and no two members wait on
+//     each other in a cycle. Only two workgroups of a pair need ever be
+//     resident together.
 //     Workgroup ids are dealt round-robin over the 8 XCDs, so the ids of one
 //     residue mod 8 draw tickets from a counter of their own and cover
-//     consecutive tiles: a pair and its neighbouring tiles then normally share
-//     one L2. Each member publishes the XCD it runs on (hardware register
-//     XCC_ID); when both members are on one XCD the exchange stays in that
-//     L2 (plain stores, loads that bypass the L1), otherwise it uses
-//     device-coherent accesses, so the result never depends on placement.
-//     Waits are bounded; on time-out the rows are written as NaN rather than
-//     hanging. Stage 1 zeroes the counters, flags and XCD words before each
-//     fold and the fold leaves them zero.
+//     consecutive tiles (the argument above then holds per counter): a pair
+//     and its neighbouring tiles normally share one L2. Each member
+//     publishes the XCD it runs on (hardware register XCC_ID); when both are
+//     on one XCD the fragments go through that L2 with plain stores and
+//     L1-bypassing loads, otherwise with device-coherent accesses.
+//     Waits are bounded: a member that gives up writes its rows as NaN
+//     rather than hanging, and counts itself in a caller-owned counter
+//     (the fold_timeouts launch option). Stage 1 zeroes the counters, flags
+//     and XCD words before each fold and the fold leaves them zero.
 //   * More members per tile (small d, so that the grid still fills the chip)
 //     each write their whole partial tile, and fold_reduce_kernel adds them in
 //     member order.
@@ -61,18 +70,6 @@ constexpr int kFoldSlots = 3;         // LDS ring slots (one step of 32 tokens e
 constexpr int kFoldMaxSplit = 32;     // members per tile (most)
 constexpr int kXcds = 8;              // gfx950: workgroup ids go round-robin over 8 XCDs
 constexpr int kFoldWGs = 256;         // one workgroup per compute unit
-constexpr int kFoldSpinLimit = 1 << 20;   // polls of a member's flag before giving up (default)
-
-// The poll limit the launches pass (process-wide; logra_set_fold_wait_limit).
-// A negative limit makes a member of a pair give up without polling, which
-// forces the time-out path from the host.
-static int g_fold_spin_limit = kFoldSpinLimit;
-
-int set_fold_spin_limit(int polls) {
-    const int prev = g_fold_spin_limit;
-    g_fold_spin_limit = polls;
-    return prev;
-}
 
 // Shape of one kernel instance. MAXB (5 or 10) bounds the 16-row blocks of a
 // tile; tiles are planned to hold MAXB or MAXB - 1 blocks where d allows,
@@ -130,7 +127,7 @@ template <int R, int MAXB, int MODE>
 __global__ __launch_bounds__(256) void fold_bf16_kernel(
     const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
     int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
-    int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit) {
+    int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit, int *__restrict__ timeouts) {
     using Sh = FoldShape<R, MAXB>;
     constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = Sh::PF, NCH = Sh::NCH;
     constexpr int kLdsRow = Sh::LDS_ROW;
@@ -452,11 +449,12 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
         return;
     }
     if (MODE == kFoldPair) {
-        // 2. raise the flag once every thread's stores are complete
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        // 2. raise the flag: the barrier orders every thread's fragment stores
+        // before thread 0's agent-scope release, which makes them visible to
+        // the other member wherever it runs
         __syncthreads();
         if (tid == 0)
-            __hip_atomic_store(flags + ti * n_split + mem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flags + ti * n_split + mem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // 3. finalize the own rows, in passes of up to kStage rows (a single pass
@@ -484,6 +482,13 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(
                         }
                         __builtin_amdgcn_s_sleep(1);
                     }
+                }
+                if (ok) {
+                    // the other member's fragments, released with its flag,
+                    // are visible to every load that follows
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                } else if (timeouts) {
+                    __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 s_word = ok;
             }
@@ -645,7 +650,8 @@ FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R) {
 
 template <int R>
 static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy, const uint16_t *P,
-                         int p_blocks, float *S, int accumulate, void *scratch, hipStream_t st) {
+                         int p_blocks, float *S, int accumulate, void *scratch, const FoldWait &wait,
+                         hipStream_t st) {
     const FoldPlan p = plan_fold_bf16(T, D, R);
     float *xbuf = static_cast<float *>(scratch);
     int *sync = reinterpret_cast<int *>(static_cast<char *>(scratch) + p.xbuf_bytes);
@@ -658,7 +664,7 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
         kernel = fold_bf16_kernel<R, 10, kFoldSingle>;
     hipLaunchKernelGGL(kernel, dim3(p.n_tiles * p.n_split), dim3(256), 0, st, dY, lddy, static_cast<int>(T),
                        static_cast<int>(D), P, p_blocks, S, xbuf, static_cast<int>(p.xbuf_bytes), sync, accumulate,
-                       p.nblk, p.n_tiles, p.n_split, p.steps_per, g_fold_spin_limit);
+                       p.nblk, p.n_tiles, p.n_split, p.steps_per, wait.spin_limit, wait.timeouts);
     if (p.n_split > 2) {
         const int64_t n = D * R;
         hipLaunchKernelGGL(fold_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, xbuf, p.n_split, n, S,
@@ -669,12 +675,12 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
 
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
-                                  void *scratch, hipStream_t st) {
+                                  void *scratch, const FoldWait &wait, hipStream_t st) {
     switch (R) {
-    case 32: return fold_r<32>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
-    case 64: return fold_r<64>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
-    case 128: return fold_r<128>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
-    case 256: return fold_r<256>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, st);
+    case 32: return fold_r<32>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, wait, st);
+    case 64: return fold_r<64>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, wait, st);
+    case 128: return fold_r<128>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, wait, st);
+    case 256: return fold_r<256>(T, D, dY, lddy, P, p_blocks, S, accumulate, scratch, wait, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -32,12 +32,17 @@ namespace logra {
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
 __device__ __forceinline__ void gram_body(uint64_t key, int R, int K, uint16_t *__restrict__ M,
-                                          int *__restrict__ counter, int bx, int by) {
+                                          int *__restrict__ counter, uint64_t *__restrict__ slots, int n_slots,
+                                          int bx, int by) {
     __shared__ uint64_t wl[16][kGramChunk + 1];
     __shared__ uint64_t wm[16][kGramChunk + 1];
     const int tid = threadIdx.x;
-    // the rowsq kernel that follows counts its workgroups from zero
-    if (bx == 0 && by == 0 && tid == 0) *counter = 0;
+    // the rowsq kernel that follows counts its workgroups from zero and
+    // finds their partials by the mark each one sets in its slot
+    if (bx == 0 && by == 0) {
+        if (tid == 0) *counter = 0;
+        for (int i = tid; i < n_slots; i += 256) slots[i] = 0;
+    }
     const int l0 = by * 16, m0 = bx * 16;
     const int tl = tid >> 4, tm = tid & 15;
     const int nb = (K + 63) / 64;
@@ -69,8 +74,9 @@ __device__ __forceinline__ void gram_body(uint64_t key, int R, int K, uint16_t *
 }
 
 __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
-                                                   int *__restrict__ counter) {
-    gram_body(key, R, K, M, counter, blockIdx.x, blockIdx.y);
+                                                   int *__restrict__ counter, uint64_t *__restrict__ slots,
+                                                   int n_slots) {
+    gram_body(key, R, K, M, counter, slots, n_slots, blockIdx.x, blockIdx.y);
 }
 
 // rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
@@ -85,19 +91,26 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
 // each with the fp32 S entries of the same (i, m), also accumulating the
 // squares of those entries: every wave thus covers its m range of both sums,
 // and the four waves' partials are added per row in wave order. The
-// controller's sum ends in the same kernel: each workgroup stores its
-// partial with a device-coherent store, waits for it, and counts itself in;
-// the last one to arrive adds all partials in index order (fixed, so the
-// result does not depend on the arrival order) and clears the counter.
+// controller's sum ends in the same kernel: each workgroup publishes its
+// partial as one 64-bit agent-scope atomic store of (mark << 32 | bits) into
+// its own slot, then counts itself in. The last one to arrive reads every
+// slot with 64-bit atomic loads, polling each until its mark is set (a slot
+// is a single atomic location, so a marked value is that workgroup's partial
+// of this launch: no ordering between different locations is relied on),
+// adds the partials in index order (fixed, so the result does not depend on
+// the arrival order), and clears the slots and the counter for the next
+// call. The poll is bounded; if it gives up, sqnorm is NaN.
 constexpr int kRowsqMaxBlocks = 8;   // 16-row blocks of S per workgroup (most)
 constexpr int kRowsqWGs = 256;       // target workgroups (one per compute unit)
+constexpr uint64_t kSlotMark = 1ull << 32;
+constexpr int kSlotSpinLimit = 1 << 22;   // polls of one slot before the sum gives up
 
 template <int R>
 __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, int K,
                                            const uint16_t *__restrict__ M, float c,
                                            const float *__restrict__ v, float beta2, float eps,
                                            float *__restrict__ v_new, float *__restrict__ rowsq,
-                                           float *__restrict__ partials, int bpw, int *__restrict__ counter,
+                                           uint64_t *__restrict__ slots, int bpw, int *__restrict__ counter,
                                            float *__restrict__ sqnorm, int blk, int nblk) {
     constexpr int KS = R / 32;                    // 32-wide steps of the rank
     constexpr int NB = R / 16;                    // 16-row blocks of m
@@ -203,8 +216,8 @@ __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, i
     __syncthreads();
     if (tid == 0) {
         const float pw = ((terms[0] + terms[1]) + terms[2]) + terms[3];
-        __hip_atomic_store(partials + blk, pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial is stored before the count
+        __hip_atomic_store(slots + blk, kSlotMark | __float_as_uint(pw), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = prev == nblk - 1;
         if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -213,9 +226,18 @@ __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, i
     if (!last) return;
     // sqnorm = the partials added in a fixed order: strided per thread, then a tree
     float t = 0.f;
-    for (int i = tid; i < nblk; i += 256)
-        t += __hip_atomic_load(partials + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    red[tid] = t;
+    bool ok = true;
+    for (int i = tid; i < nblk; i += 256) {
+        uint64_t w = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int spins = 0; !(w & kSlotMark) && spins < kSlotSpinLimit; ++spins) {
+            __builtin_amdgcn_s_sleep(1);
+            w = __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ok = ok && (w & kSlotMark);
+        t += __uint_as_float(static_cast<uint32_t>(w));
+        __hip_atomic_store(slots + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    red[tid] = ok ? t : __builtin_nanf("");
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
         if (tid < w) red[tid] += red[tid + w];
@@ -230,9 +252,9 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
                                                          const float *__restrict__ v, float beta2,
                                                          float eps, float *__restrict__ v_new,
                                                          float *__restrict__ rowsq,
-                                                         float *__restrict__ partials, int bpw,
+                                                         uint64_t *__restrict__ slots, int bpw,
                                                          int *__restrict__ counter, float *__restrict__ sqnorm) {
-    rowsq_body<R>(S, D, K, M, c, v, beta2, eps, v_new, rowsq, partials, bpw, counter, sqnorm, blockIdx.x,
+    rowsq_body<R>(S, D, K, M, c, v, beta2, eps, v_new, rowsq, slots, bpw, counter, sqnorm, blockIdx.x,
                   gridDim.x);
 }
 
@@ -245,7 +267,7 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
 template <int R>
 __global__ __launch_bounds__(256) void gram_batch_kernel(SqnormBatch b) {
     const SqnormItem &it = b.item[blockIdx.z];
-    gram_body(it.key, R, it.K, it.M, it.counter, blockIdx.x, blockIdx.y);
+    gram_body(it.key, R, it.K, it.M, it.counter, it.slots, it.n_wg, blockIdx.x, blockIdx.y);
 }
 
 template <int R>
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(256) void rowsq_batch_kernel(SqnormBatch b) {
     int j = 0;
     while (j + 1 < b.n && static_cast<int>(blockIdx.x) >= b.item[j + 1].wg_begin) ++j;
     const SqnormItem &it = b.item[j];
-    rowsq_body<R>(it.S, it.D, it.K, it.M, it.c, it.v, b.beta2, b.eps, it.v_new, it.rowsq, it.partials, it.bpw,
+    rowsq_body<R>(it.S, it.D, it.K, it.M, it.c, it.v, b.beta2, b.eps, it.v_new, it.rowsq, it.slots, it.bpw,
                   it.counter, b.sqnorm + j, static_cast<int>(blockIdx.x) - it.wg_begin, it.n_wg);
 }
 
@@ -268,7 +290,7 @@ SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
     p.rows_per_block = static_cast<int>(16 * bpw);
     p.n_blocks = static_cast<int>((D + p.rows_per_block - 1) / p.rows_per_block);
     const size_t align = 256;
-    p.partial_bytes = (static_cast<size_t>(p.n_blocks) * 4 + align - 1) / align * align;
+    p.partial_bytes = (static_cast<size_t>(p.n_blocks) * 8 + align - 1) / align * align;
     p.gram_bytes = (static_cast<size_t>(R) * R * 2 + align - 1) / align * align;
     p.counter_bytes = align;
     return p;
@@ -278,16 +300,17 @@ template <int R>
 static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, int parts, hipStream_t st) {
     const SqnormPlan p = plan_sqnorm_bf16(a.D, a.K, R);
     char *base = static_cast<char *>(ws);
-    float *partials = reinterpret_cast<float *>(base);
+    uint64_t *slots = reinterpret_cast<uint64_t *>(base);
     uint16_t *M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
     int *counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
     const int K = static_cast<int>(a.K);
     if (parts & kSqnormGram)
-        hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter);
+        hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter, slots,
+                           p.n_blocks);
     if (parts & kSqnormRows)
         hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
                            static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out,
-                           partials, p.rows_per_block / 16, counter, a.sqnorm);
+                           slots, p.rows_per_block / 16, counter, a.sqnorm);
     return hipGetLastError();
 }
 

@@ -34,25 +34,25 @@ struct FoldPlan {
     size_t sync_bytes = 0;
 };
 FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
-// Sets the polls a fold member makes for its partner before it gives up and
-// writes its rows as NaN; returns the previous limit. Negative: give up at once.
-int set_fold_spin_limit(int polls);
-// Sets how many independent sketch calls run at once (the projection sizes
-// its workgroups for that share of the chip); returns the previous value.
-int set_sketch_concurrency(int n);
-// Sets how many apply calls run at once (pass 2 sizes its grid for that);
-// returns the previous value.
-int set_apply_concurrency(int n);
+
+// How a fold member waits for its partner: at most spin_limit polls
+// (negative: give up at once), then its rows are written as NaN and
+// *timeouts (device, may be null) is incremented.
+struct FoldWait {
+    int spin_limit = 1 << 20;
+    int *timeouts = nullptr;
+};
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
-                                  void *scratch, hipStream_t st);
+                                  void *scratch, const FoldWait &wait, hipStream_t st);
 size_t workspace_sketch_f32(int64_t T, int64_t R);
 int apply_blocks_f32(int64_t D);
 
-// Workspace of apply pass 1 with bf16 compute: per-workgroup partials of the
-// controller's reduction, then the r x r Gram matrix of the signs (bf16),
-// then the counter the last workgroup is found with (zeroed by the Gram
-// kernel, left zero).
+// Workspace of apply pass 1 with bf16 compute: one 64-bit slot per
+// workgroup for its partial of the controller's reduction (a mark in the
+// high word, the float's bits in the low word), then the r x r Gram matrix
+// of the signs (bf16), then the counter the last workgroup is found with
+// (slots and counter zeroed by the Gram kernel and left zero).
 struct SqnormPlan {
     int n_blocks = 0;         // workgroups of rowsq_gram_kernel
     int rows_per_block = 0;   // rows of S each of them owns
@@ -65,11 +65,13 @@ SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R);
 hipError_t launch_sign_words(uint64_t key, int R, int K, uint64_t *words, hipStream_t st);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t st);
 
-// stage 1: P = c X Sigma^T into the workspace; stage 2: S (+)= dY^T P from it.
+// stage 1: P = c X Sigma^T into the workspace (concurrency: independent
+// sketch calls the caller runs at once, this one included); stage 2:
+// S (+)= dY^T P from it.
 hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t key, float c,
-                               const uint16_t *X, int64_t ldx, void *ws, hipStream_t st);
+                               const uint16_t *X, int64_t ldx, void *ws, int concurrency, hipStream_t st);
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                            float *S, int accumulate, void *ws, hipStream_t st);
+                            float *S, int accumulate, void *ws, const FoldWait &wait, hipStream_t st);
 hipError_t launch_project_f32(int R, int64_t T, int64_t K, uint64_t key, float c, const float *X,
                               int64_t ldx, void *ws, hipStream_t st);
 hipError_t launch_fold_f32(int R, int64_t T, int64_t D, const float *dY, int64_t lddy, float *S,
@@ -103,7 +105,7 @@ struct SqnormItem {
     float *v_new = nullptr;
     float *rowsq = nullptr;        // may be null
     uint16_t *M = nullptr;         // Gram matrix in the item's workspace slice
-    float *partials = nullptr;
+    uint64_t *slots = nullptr;     // per-workgroup partial slots
     int *counter = nullptr;
     uint64_t key = 0;
     float c = 0.f;
@@ -125,7 +127,8 @@ hipError_t launch_sqnorm_batch_bf16(int R, const SqnormBatch &b, hipStream_t st)
 // only on the key, k and r) and the row pass that reads it.
 constexpr int kSqnormGram = 1, kSqnormRows = 2;
 hipError_t launch_sqnorm_bf16(const ApplyArgs &a, void *ws, hipStream_t st, int parts = kSqnormGram | kSqnormRows);
-hipError_t launch_rowadam_bf16(const ApplyArgs &a, hipStream_t st);
+// concurrency: apply calls the caller runs at once, this one included.
+hipError_t launch_rowadam_bf16(const ApplyArgs &a, int concurrency, hipStream_t st);
 // fp32 compute: mode 0 = pass 1 (rowsq + partials), mode 1 = pass 2 (W and v).
 hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);
 hipError_t launch_sqnorm_final(const float *partials, int n, float *out, hipStream_t st);

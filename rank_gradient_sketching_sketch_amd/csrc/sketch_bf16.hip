@@ -39,17 +39,6 @@ constexpr int kS1Prefetch = 2;    // steps of X held in registers ahead of use (
 constexpr int kS1TileBytes = 147456;   // LDS for the reduction tiles (8 waves x 128 x 36 fp32)
 constexpr int kS1MinWGs64 = 256;  // workgroups (times the concurrency) from which 64-token ones are used
 
-// Independent sketch calls the caller keeps in flight on separate streams
-// (process-wide; logra_set_sketch_concurrency). The projection picks its
-// workgroup shape for a 1/n share of the chip.
-static int g_sketch_concurrency = 1;
-
-int set_sketch_concurrency(int n) {
-    const int prev = g_sketch_concurrency;
-    g_sketch_concurrency = n;
-    return prev;
-}
-
 template <int R>
 struct Stage1Shape {
     static constexpr int RT = R < 128 ? R : 128;   // sign columns per workgroup
@@ -245,18 +234,18 @@ Stage1Plan plan_stage1_bf16(int64_t T, int64_t K, int R) {
 
 template <int R>
 static hipError_t project_bf16_r(int64_t T, int64_t D, int64_t K, uint64_t key, float c, const uint16_t *X,
-                                 int64_t ldx, void *ws, hipStream_t st) {
+                                 int64_t ldx, void *ws, int concurrency, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
     const FoldPlan f = plan_fold_bf16(T, D, R);
     uint16_t *P = static_cast<uint16_t *>(ws);
     int *sync = reinterpret_cast<int *>(static_cast<char *>(ws) + p.p_bytes + f.xbuf_bytes);
     // 64-token workgroups where they still give a workgroup per compute
-    // unit of this call's share of the chip, and never fewer than half a
-    // chip's worth of them (with four streams, 64 workgroups of 64 tokens
-    // lost to 128 of 32), else 32-token ones
+    // unit of this call's share of the chip (1 / concurrency of it), and
+    // never fewer than half a chip's worth of them (with four streams, 64
+    // workgroups of 64 tokens lost to 128 of 32), else 32-token ones
     const int wg64 = (p.t_blocks + 1) / 2;
     const int64_t n64 = static_cast<int64_t>(wg64) * p.col_tiles;
-    const bool tall = n64 * g_sketch_concurrency >= kS1MinWGs64 && 2 * n64 >= kS1MinWGs64;
+    const bool tall = n64 * concurrency >= kS1MinWGs64 && 2 * n64 >= kS1MinWGs64;
     auto kernel = tall ? stage1_bf16_kernel<R, 4> : stage1_bf16_kernel<R, 2>;
     hipLaunchKernelGGL(kernel, dim3(tall ? wg64 : p.t_blocks, p.col_tiles), dim3(64 * kS1Waves), 0, st, X, ldx,
                        static_cast<int>(T), static_cast<int>(K), key, c, P, p.t_blocks, sync, f.sync_words);
@@ -265,32 +254,32 @@ static hipError_t project_bf16_r(int64_t T, int64_t D, int64_t K, uint64_t key, 
 
 template <int R>
 static hipError_t fold_bf16_r(int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                              float *S, int accumulate, void *ws, hipStream_t st) {
+                              float *S, int accumulate, void *ws, const FoldWait &wait, hipStream_t st) {
     const Stage1Plan p = plan_stage1_bf16(T, K, R);
     char *base = static_cast<char *>(ws);
     const uint16_t *P = reinterpret_cast<const uint16_t *>(base);
     void *scratch = base + p.p_bytes;   // exchange buffer, then the sync words
-    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, p.t_blocks, S, accumulate, scratch, st);
+    return launch_fold_bf16_tiles(R, T, D, dY, lddy, P, p.t_blocks, S, accumulate, scratch, wait, st);
 }
 
 hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t key, float c,
-                               const uint16_t *X, int64_t ldx, void *ws, hipStream_t st) {
+                               const uint16_t *X, int64_t ldx, void *ws, int concurrency, hipStream_t st) {
     switch (R) {
-    case 32: return project_bf16_r<32>(T, D, K, key, c, X, ldx, ws, st);
-    case 64: return project_bf16_r<64>(T, D, K, key, c, X, ldx, ws, st);
-    case 128: return project_bf16_r<128>(T, D, K, key, c, X, ldx, ws, st);
-    case 256: return project_bf16_r<256>(T, D, K, key, c, X, ldx, ws, st);
+    case 32: return project_bf16_r<32>(T, D, K, key, c, X, ldx, ws, concurrency, st);
+    case 64: return project_bf16_r<64>(T, D, K, key, c, X, ldx, ws, concurrency, st);
+    case 128: return project_bf16_r<128>(T, D, K, key, c, X, ldx, ws, concurrency, st);
+    case 256: return project_bf16_r<256>(T, D, K, key, c, X, ldx, ws, concurrency, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
-                            float *S, int accumulate, void *ws, hipStream_t st) {
+                            float *S, int accumulate, void *ws, const FoldWait &wait, hipStream_t st) {
     switch (R) {
-    case 32: return fold_bf16_r<32>(T, D, K, dY, lddy, S, accumulate, ws, st);
-    case 64: return fold_bf16_r<64>(T, D, K, dY, lddy, S, accumulate, ws, st);
-    case 128: return fold_bf16_r<128>(T, D, K, dY, lddy, S, accumulate, ws, st);
-    case 256: return fold_bf16_r<256>(T, D, K, dY, lddy, S, accumulate, ws, st);
+    case 32: return fold_bf16_r<32>(T, D, K, dY, lddy, S, accumulate, ws, wait, st);
+    case 64: return fold_bf16_r<64>(T, D, K, dY, lddy, S, accumulate, ws, wait, st);
+    case 128: return fold_bf16_r<128>(T, D, K, dY, lddy, S, accumulate, ws, wait, st);
+    case 256: return fold_bf16_r<256>(T, D, K, dY, lddy, S, accumulate, ws, wait, st);
     default: return hipErrorInvalidValue;
     }
 }

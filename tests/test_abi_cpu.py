@@ -40,46 +40,80 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
-    assert B.logra_abi_version() == 2
+    assert B.logra_abi_version() == 3
     assert B.logra_status_string(0) == "LOGRA_OK"
     assert B.logra_status_string(3) == "LOGRA_ERR_WORKSPACE"
     assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
 
 
-def test_fold_wait_limit_round_trip(lib):
-    # host-side setting only: returns the previous limit, default 1 << 20
+def test_no_process_wide_settings(lib):
+    # ABI 3 keeps no mutable global state: the former process-wide setters
+    # are gone, their settings travel with each call in logra_launch_opts
+    for name in ("logra_set_fold_wait_limit", "logra_set_sketch_concurrency", "logra_set_apply_concurrency"):
+        assert not hasattr(lib, name), name
+    src = os.path.join(ROOT, "rank_gradient_sketching_sketch_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        for line in open(os.path.join(src, f)):
+            # a static declaration that is neither a function nor a constant
+            # is mutable state shared by every call
+            if line.startswith("static ") and "(" not in line.split("=")[0]:
+                assert line.startswith(("static constexpr", "static const ")), (f, line)
+
+
+def test_launch_opts_validation(lib):
+    # out-of-range hints and a non-zero reserved field are refused before any
+    # launch; NULL and a zeroed struct are the defaults
     from rank_gradient_sketching_sketch_amd import binding as B
-    prev = B.logra_set_fold_wait_limit(5)
-    try:
-        assert prev == 1 << 20
-        assert B.logra_set_fold_wait_limit(-1) == 5
-        assert lib.logra_set_fold_wait_limit(7, None) == 0   # previous may be NULL
-    finally:
-        assert B.logra_set_fold_wait_limit(prev) == 7
+    m = _m()
+    r = ctypes.byref
+    T, ws = 4, 1 << 20
+
+    def acc(o):
+        return lib.logra_sketch_accumulate(r(m), T, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, ws, o, None)
+
+    def bad_opts(**kw):
+        o = B.LaunchOpts()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return r(o)
+
+    assert acc(bad_opts(sketch_concurrency=-1)) == 1
+    assert acc(bad_opts(sketch_concurrency=257)) == 1
+    assert acc(bad_opts(apply_concurrency=300)) == 1
+    assert acc(bad_opts(reserved=1)) == 1
+    assert lib.logra_sketch_project(r(m), T, 1, FAKE, 128, FAKE, ws, bad_opts(reserved=2), None) == 1
+    assert lib.logra_sketch_fold(r(m), T, 1, FAKE, 64, FAKE, 0, FAKE, ws, bad_opts(sketch_concurrency=-5),
+                                 None) == 1
+    assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 128, ctypes.c_float(1e-3), ctypes.c_float(1.0),
+                                   ctypes.c_float(1e-8), bad_opts(apply_concurrency=-1), None) == 1
+    # the option checks come first: a bad option with T == 0 (no launch) is still refused
+    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0,
+                                       bad_opts(reserved=7), None) == 1
+    # valid options with nothing to launch: accepted
+    o = B.LaunchOpts(sketch_concurrency=4, apply_concurrency=3, fold_wait_limit=-1)
+    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, r(o), None) == 0
+    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None, None) == 0
 
 
-def test_sketch_concurrency_round_trip(lib):
-    # host-side setting only: default 1, previous value returned, range checked
+def test_projection_view_overflow_is_unsupported(lib):
+    # The projection (ceil(T/32) blocks x 32 tokens x r, bf16) is read through
+    # a 32-bit buffer view: with a small d, X and dY fit their views while
+    # the projection would not, which must be refused, not wrapped.
     from rank_gradient_sketching_sketch_amd import binding as B
-    prev = B.logra_set_sketch_concurrency(4)
-    try:
-        assert prev == 1
-        assert lib.logra_set_sketch_concurrency(0, None) == 1      # INVALID_ARGUMENT
-        assert lib.logra_set_sketch_concurrency(257, None) == 1
-        assert B.logra_set_sketch_concurrency(2) == 4               # unchanged by the errors
-    finally:
-        assert B.logra_set_sketch_concurrency(prev) == 2
-
-
-def test_apply_concurrency_round_trip(lib):
-    from rank_gradient_sketching_sketch_amd import binding as B
-    prev = B.logra_set_apply_concurrency(3)
-    try:
-        assert prev == 1
-        assert lib.logra_set_apply_concurrency(0, None) == 1      # INVALID_ARGUMENT
-        assert B.logra_set_apply_concurrency(2) == 3
-    finally:
-        assert B.logra_set_apply_concurrency(prev) == 2
+    r = ctypes.byref
+    T = (1 << 22)          # 2 * (T + 32) * 256 >= 2^31
+    m = B.MatrixDesc(8, 8, 256, 0, 0, 0)
+    assert 2 * T * 8 < (1 << 31)                       # X and dY views fit
+    assert lib.logra_sketch_accumulate(r(m), T, 1, FAKE, 8, FAKE, 8, FAKE, 0, FAKE, 1 << 40, None, None) == 2
+    assert lib.logra_sketch_project(r(m), T, 1, FAKE, 8, FAKE, 1 << 40, None, None) == 2
+    assert lib.logra_sketch_fold(r(m), T, 1, FAKE, 8, FAKE, 0, FAKE, 1 << 40, None, None) == 2
+    # one 32-token block fewer than the limit needs at r = 256 passes validation
+    # up to the workspace check (WORKSPACE: the fake workspace size is too small)
+    T_ok = (1 << 22) - 64
+    assert lib.logra_sketch_project(r(m), T_ok, 1, FAKE, 8, FAKE, 16, None, None) == 3
+    # the same T at r = 128 fits
+    m128 = B.MatrixDesc(8, 8, 128, 0, 0, 0)
+    assert lib.logra_sketch_project(r(m128), T, 1, FAKE, 8, FAKE, 16, None, None) == 3
 
 
 def _m(d=64, k=128, r=32):
@@ -94,24 +128,24 @@ def test_validation_errors_return_before_launch(lib):
     m = _m()
     r = ctypes.byref
     # null descriptor / null S
-    assert lib.logra_sketch_accumulate(None, 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
-    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, None, 0, FAKE, 1 << 20, None) == 1
+    assert lib.logra_sketch_accumulate(None, 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, None, 0, FAKE, 1 << 20, None, None) == 1
     # negative T, ld < cols, misaligned pointer
-    assert lib.logra_sketch_accumulate(r(m), -1, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
-    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 100, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), -1, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None, None) == 1
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 100, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None, None) == 1
     assert lib.logra_sketch_accumulate(r(m), 4, 1, ctypes.c_void_p(0x10002), 128, FAKE, 64, FAKE, 0,
-                                       FAKE, 1 << 20, None) == 1
+                                       FAKE, 1 << 20, None, None) == 1
     # unsupported rank / dtype / shape on the bf16 path
     m48 = _m(r=48)
-    assert lib.logra_sketch_accumulate(r(m48), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 2
-    assert lib.logra_sketch_accumulate(r(m), 4, 7, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None) == 2
+    assert lib.logra_sketch_accumulate(r(m48), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None, None) == 2
+    assert lib.logra_sketch_accumulate(r(m), 4, 7, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 1 << 20, None, None) == 2
     m_odd = _m(d=60)
-    assert lib.logra_sketch_accumulate(r(m_odd), 4, 1, FAKE, 128, FAKE, 60, FAKE, 0, FAKE, 1 << 20, None) == 2
+    assert lib.logra_sketch_accumulate(r(m_odd), 4, 1, FAKE, 128, FAKE, 60, FAKE, 0, FAKE, 1 << 20, None, None) == 2
     # workspace too small / missing
-    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 16, None) == 3
-    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, None, 1 << 20, None) == 3
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, FAKE, 16, None, None) == 3
+    assert lib.logra_sketch_accumulate(r(m), 4, 1, FAKE, 128, FAKE, 64, FAKE, 0, None, 1 << 20, None, None) == 3
     # T == 0 with accumulate: nothing to do, no launch
-    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None) == 0
+    assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None, None) == 0
     # apply passes: beta2 out of range, eps < 0, nulls, v' aliasing v, unsupported
     V2 = ctypes.c_void_p(0x20000)
     def sq(beta2, eps, v_new=V2, sqn=FAKE, ws_bytes=1 << 20, mm=m):
@@ -125,13 +159,13 @@ def test_validation_errors_return_before_launch(lib):
     assert sq(0.9, 1e-8, ws_bytes=0) == 3
     assert sq(0.9, 1e-8, mm=m48) == 2
     assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 100, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 1
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None, None) == 1
     assert lib.logra_rowadam_apply(r(m), 1, FAKE, None, FAKE, 1, 128, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 1
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None, None) == 1
     assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 128, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(-1.0), None) == 1
+                                   ctypes.c_float(1.0), ctypes.c_float(-1.0), None, None) == 1
     assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 5, 128, ctypes.c_float(1e-3),
-                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None) == 2
+                                   ctypes.c_float(1.0), ctypes.c_float(1e-8), None, None) == 2
     assert lib.logra_sign_words(None, FAKE, None) == 1
 
 

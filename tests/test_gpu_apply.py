@@ -27,7 +27,7 @@ def _state(seed, d, k, r, s_std=1e-2):
     return S, v, W
 
 
-def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev):
+def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev, opts=None):
     S_d, v_d, W_d = S.to(dev), v.clone().to(dev), W.clone().to(dev)
     v_new = torch.empty(m.d, dtype=torch.float32, device=dev)
     rowsq = torch.empty(m.d, dtype=torch.float32, device=dev)
@@ -35,7 +35,7 @@ def _run(m, compute, S, v, W, lr, scale, beta2, eps, dev):
     B.logra_update_sqnorm(m, compute, S_d, v_d, beta2, eps, v_new, sq, rowsq)
     torch.cuda.synchronize()
     rowsq_h, sq_h = rowsq.cpu(), sq.item()
-    B.logra_rowadam_apply(m, compute, S_d, v_new, W_d, lr, scale, eps)
+    B.logra_rowadam_apply(m, compute, S_d, v_new, W_d, lr, scale, eps, opts=opts)
     torch.cuda.synchronize()
     # pass 1 leaves v as it was
     assert torch.equal(v_d.cpu(), v)
@@ -86,7 +86,7 @@ def test_apply_bf16_compute_matches_oracle(d, k, r, wdt):
         say("  dW %.2e" % e_w)
         assert e_w < BF16_TOL
     else:
-        ok, worst = bf16_w_check(W_new.double().numpy(), ref["W_new"], W0)
+        ok, worst, _ = bf16_w_check(W_new.double().numpy(), ref["W_new"], W0)
         say("  bf16 W worst error / allowed %.3f" % worst)
         assert ok
 
@@ -132,16 +132,13 @@ def test_apply_concurrency_hint_keeps_parity(d, k, r):
     S, v, W = _state(7 * d + k, d, k, r)
     W = W.to(torch.bfloat16)
     lr, scale, beta2, eps = 1e-3, 0.8, 0.999, 1e-8
-    prev = B.logra_set_apply_concurrency(3)
-    try:
-        _, _, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, W, lr, scale, beta2, eps, dev)
-    finally:
-        assert B.logra_set_apply_concurrency(prev) == 3
+    _, _, v_new, W_new = _run(m, B.LOGRA_BF16, S, v, W, lr, scale, beta2, eps, dev,
+                              opts=B.LaunchOpts(apply_concurrency=3))
     A = oracle.sign_matrix(6, d, k, r, k)
     ref = oracle.rowadam_rows(S.double().numpy(), A, v.double().numpy(), W.double().numpy(),
                               beta2=f32(beta2), eps=f32(eps), lr=f32(lr), scale=f32(scale))
     assert rel_err(v_new.double().numpy(), ref["v_new"]) < BF16_TOL
-    ok, worst = bf16_w_check(W_new.double().numpy(), ref["W_new"], W.double().numpy())
+    ok, worst, _ = bf16_w_check(W_new.double().numpy(), ref["W_new"], W.double().numpy())
     say("  bf16 W worst error / allowed %.3f" % worst)
     assert ok
 
@@ -246,7 +243,7 @@ def test_policy_sync_replica_matches_trainer(wdt):
     if wdt == torch.float32:
         assert w_update_err(to_f64(W_replica), ref["W_new"], W0) < BF16_TOL
     else:
-        ok, _ = bf16_w_check(to_f64(W_replica), ref["W_new"], W0)
+        ok, _, _ = bf16_w_check(to_f64(W_replica), ref["W_new"], W0)
         assert ok
 
 

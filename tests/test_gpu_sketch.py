@@ -32,10 +32,10 @@ def test_sign_words_bit_exact(seed, step, mid, r, k):
     assert np.array_equal(got, oracle.sign_words(seed, step, mid, r, k))
 
 
-def _run_sketch(m, X_list, dY_list, dev):
+def _run_sketch(m, X_list, dY_list, dev, opts=None):
     S = torch.full((m.d, m.r), float("nan"), dtype=torch.float32, device=dev)
     for n, (X, dY) in enumerate(zip(X_list, dY_list)):
-        B.logra_sketch_accumulate(m, X.to(dev), dY.to(dev), S, accumulate=n > 0)
+        B.logra_sketch_accumulate(m, X.to(dev), dY.to(dev), S, accumulate=n > 0, opts=opts)
     torch.cuda.synchronize()
     return S
 
@@ -142,12 +142,13 @@ def test_fold_twice_from_one_projection():
     assert torch.equal(S_acc, S1)
 
 
-def test_fold_wait_timeout_writes_nan_and_recovers():
+def test_fold_wait_timeout_writes_nan_counts_and_recovers():
     # Forced from the host: with a negative wait limit the two members of
-    # every tile give up on each other at once and write their rows as NaN
-    # (every kernel still runs to its end). With the default limit back, a
-    # second fold from the same projection and workspace gives the exact
-    # result: the timed-out fold left its sync words usable.
+    # every tile give up on each other at once, write their rows as NaN and
+    # count themselves in the caller's time-out counter (every kernel still
+    # runs to its end). With the default limit, a second fold from the same
+    # projection and workspace gives the exact result and counts nothing:
+    # the timed-out fold left its sync words usable.
     dev = device()
     T, d, k, r = 320, 8208, 96, 256   # d >= 8192: tiles over two token halves
     say("fold wait time-out", T, d, k, r)
@@ -158,18 +159,45 @@ def test_fold_wait_timeout_writes_nan_and_recovers():
     S_ref = torch.empty(d, r, device=dev)
     B.logra_sketch_accumulate(m, X, dY, S_ref, accumulate=False)
     S = torch.zeros(d, r, device=dev)
+    timeouts = torch.zeros(1, dtype=torch.int32, device=dev)
     B.logra_sketch_project(m, X, ws)
-    prev = B.logra_set_fold_wait_limit(-1)
-    try:
-        B.logra_sketch_fold(m, dY, S, False, ws)
-        torch.cuda.synchronize()
-    finally:
-        assert B.logra_set_fold_wait_limit(prev) == -1
-    assert prev == 1 << 20
+    B.logra_sketch_fold(m, dY, S, False, ws, opts=B.LaunchOpts(fold_wait_limit=-1, fold_timeouts=timeouts))
+    torch.cuda.synchronize()
     assert torch.isnan(S).all()
-    B.logra_sketch_fold(m, dY, S, False, ws)
+    # every member of every tile gave up once (128 tiles x 2 members here)
+    plan_members = 256
+    assert timeouts.item() == plan_members
+    timeouts.zero_()
+    B.logra_sketch_fold(m, dY, S, False, ws, opts=B.LaunchOpts(fold_timeouts=timeouts))
     torch.cuda.synchronize()
     assert torch.equal(S, S_ref)
+    assert timeouts.item() == 0
+
+
+def test_fold_options_are_per_call():
+    # Two folds from one projection, one with a negative wait limit, one with
+    # the defaults, launched back to back on two streams: each gets its own
+    # setting (no process-wide state), whatever order they run in.
+    dev = device()
+    T, d, k, r = 320, 8208, 96, 256
+    m = B.MatrixDesc(d, k, r, 1, 2, 4)
+    X, dY = inputs.random_case(79, T, d, k, dtype=torch.bfloat16, dy_std=1e-2)
+    X, dY = X.to(dev), dY.to(dev)
+    S_ref = torch.empty(d, r, device=dev)
+    B.logra_sketch_accumulate(m, X, dY, S_ref, accumulate=False)
+    ws = [torch.empty(B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+          for _ in range(2)]
+    S = [torch.zeros(d, r, device=dev) for _ in range(2)]
+    cnt = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(2)]
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream(device=dev)]
+    streams[1].wait_stream(streams[0])
+    for i, lim in enumerate((-1, 0)):
+        B.logra_sketch_project(m, X, ws[i], stream=streams[i])
+        B.logra_sketch_fold(m, dY, S[i], False, ws[i], stream=streams[i],
+                            opts=B.LaunchOpts(fold_wait_limit=lim, fold_timeouts=cnt[i]))
+    torch.cuda.synchronize()
+    assert torch.isnan(S[0]).all() and cnt[0].item() == 256
+    assert torch.equal(S[1], S_ref) and cnt[1].item() == 0
 
 
 @pytest.mark.parametrize("n", [1, 4])
@@ -183,11 +211,7 @@ def test_sketch_concurrency_hint_keeps_parity(n):
     say("sketch concurrency", n, T, d, k, r)
     m = B.MatrixDesc(d, k, r, seed=9, step=n, matrix_id=d)
     X, dY = inputs.random_case(4242 + n, T, d, k, dtype=torch.bfloat16, dy_std=1e-2, outlier_cols=2)
-    prev = B.logra_set_sketch_concurrency(n)
-    try:
-        S = _run_sketch(m, [X], [dY], dev)
-    finally:
-        assert B.logra_set_sketch_concurrency(prev) == n
+    S = _run_sketch(m, [X], [dY], dev, opts=B.LaunchOpts(sketch_concurrency=n))
     err = rownorm_err(to_f64(S), _ref_sketch(m, [X], [dY]))
     say("  S rownorm err %.3e" % err)
     assert err < BF16_TOL

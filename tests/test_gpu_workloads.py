@@ -81,7 +81,7 @@ def _step_and_check(wl, spec, step, st, dev, mbs, T, tol, data_seed=0):
     st["v"] = v_new   # the update was applied: v' is the next step's v
     W_new = to_f64(W)[rows]
     if W.dtype == torch.bfloat16:
-        w_ok, _ = bf16_w_check(W_new, ref["W_new"], st["W_ref"], steps=step + 1)
+        w_ok, _, st["allow"] = bf16_w_check(W_new, ref["W_new"], st["W_ref"], prior=st.get("allow"))
         ref32 = oracle.rowadam_rows(S_ref, A, st["v_ref"], st["W32_ref"], **hp)
         e_w = w_update_err(to_f64(W32)[rows], ref32["W_new"], st["W32_ref"])
         st["W32_ref"] = ref32["W_new"]

@@ -125,3 +125,19 @@ def test_pages_printed_figures_arithmetic():
     r = int(vals["rank"])
     d, k = 18944, 3584
     assert (d * k) / (d * r) == 14.0
+
+
+def test_project_matmul_equals_the_loops():
+    # The library-matmul form of P = X A^T that the layer-stack tests use
+    # gives the plain loops' result up to fp64 rounding, on a ragged shape
+    # with outlier columns; and it reproduces the one-hot probe exactly
+    # (X = I gives A^T).
+    rng = np.random.default_rng(11)
+    T, k, r = 37, 203, 24
+    X = rng.standard_normal((T, k))
+    X[:, [3, 90]] *= 10.0
+    A = oracle.sign_matrix(2, 5, 7, r, k)
+    P1 = oracle.project(X, A)
+    P2 = oracle.project_matmul(X, A)
+    assert np.abs(P1 - P2).max() <= 1e-12 * np.abs(P1).max()
+    assert np.array_equal(oracle.project_matmul(np.eye(k), A), A.T)
