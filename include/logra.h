@@ -324,6 +324,35 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
                                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * logra_update_sqnorm_noalloc -- logra_update_sqnorm for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same pass 1, the same kernels and
+ * bit-identical outputs, with the workspace taken from a scratch array the
+ * library holds in device memory instead of from an argument.
+ * Arguments, requirements and errors: as logra_update_sqnorm, without ws and
+ * ws_bytes. The call allocates nothing and calls no allocating routine.
+ * Limit: the workspace logra_update_sqnorm would need for m
+ *   (logra_sqnorm_workspace_bytes(m, compute_dtype)) must not exceed
+ *   LOGRA_NOALLOC_SCRATCH_BYTES (512 KiB: on the bf16 path d up to 6,287,360
+ *   rows at r = 256 and 8,351,744 at r = 32; on the fp32 path d up to
+ *   1,048,576 rows at any r); larger m returns LOGRA_ERR_WORKSPACE and
+ *   launches nothing.
+ * Sharing: each device holds one copy of the scratch until the process ends,
+ *   and every call on that device uses it; the call leaves it ready for the
+ *   next one (it zeroes what must start at zero itself). Calls that overlap
+ *   in time on one device (other streams, other host threads) race on it
+ *   and give undefined results: order them (same stream, or events).
+ * Errors: as logra_update_sqnorm; WORKSPACE above the limit; HIP if the
+ *   current device cannot be queried.
+ */
+#define LOGRA_NOALLOC_SCRATCH_BYTES (512u * 1024u)
+logra_status logra_update_sqnorm_noalloc(const logra_matrix *m, int compute_dtype,
+                                         const float *S, const float *v,
+                                         float beta2, float eps,
+                                         float *v_new, float *rowsq, float *sqnorm,
+                                         void *stream);
+
+/*
  * logra_rowadam_apply -- apply pass 2:
  *   W_ij <- W_ij - lr * scale * Ghat_ij / (sqrt(v_new_i) + eps)
  * with Ghat = S A rebuilt tile by tile and v_new the second moment that

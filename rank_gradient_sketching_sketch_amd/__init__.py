@@ -12,7 +12,7 @@ __all__ = [
     "logra_sketch_workspace_bytes", "logra_sketch_accumulate",
     "logra_sketch_project", "logra_sketch_fold", "LaunchOpts",
     "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
-    "logra_sqnorm_prepare", "logra_update_sqnorm_prepared",
+    "logra_sqnorm_prepare", "logra_update_sqnorm_prepared", "logra_update_sqnorm_noalloc",
     "logra_sqnorm_batch_workspace_bytes", "logra_update_sqnorm_batch",
     "logra_kl_budget_at", "logra_kl_step_scale", "KLBudget",
     "LograError", "MatrixDesc", "library_path", "load_library",

@@ -109,6 +109,8 @@ def load_library():
     lib.logra_update_sqnorm.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
     lib.logra_update_sqnorm_prepared.restype = i32
     lib.logra_update_sqnorm_prepared.argtypes = [D, i32, P, P, f32, f32, P, P, P, P, sz, P]
+    lib.logra_update_sqnorm_noalloc.restype = i32
+    lib.logra_update_sqnorm_noalloc.argtypes = [D, i32, P, P, f32, f32, P, P, P, P]
     lib.logra_sqnorm_prepare.restype = i32
     lib.logra_sqnorm_prepare.argtypes = [D, i32, P, sz, P]
     lib.logra_rowadam_apply.restype = i32
@@ -234,6 +236,20 @@ def logra_update_sqnorm(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: t
         ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
         _ptr(v_new), _ptr(rowsq), _ptr(sqnorm), _ptr(ws), ws_bytes, _stream(stream)),
         "logra_update_sqnorm")
+
+
+NOALLOC_SCRATCH_BYTES = 512 * 1024
+
+
+def logra_update_sqnorm_noalloc(m: MatrixDesc, compute_dtype: int, S: torch.Tensor, v: torch.Tensor,
+                                beta2: float, eps: float, v_new: torch.Tensor, sqnorm: torch.Tensor,
+                                rowsq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Pass 1 as logra_update_sqnorm, with the library's own device scratch
+    instead of a workspace (nothing is allocated); calls on one device must
+    not overlap in time."""
+    _check(load_library().logra_update_sqnorm_noalloc(
+        ctypes.byref(m), int(compute_dtype), _ptr(S), _ptr(v), float(beta2), float(eps),
+        _ptr(v_new), _ptr(rowsq), _ptr(sqnorm), _stream(stream)), "logra_update_sqnorm_noalloc")
 
 
 def logra_sqnorm_prepare(m: MatrixDesc, compute_dtype: int, ws: torch.Tensor, stream=None) -> None:

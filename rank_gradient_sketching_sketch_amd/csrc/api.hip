@@ -4,6 +4,8 @@
 // every buffer, workspace included, comes from the caller.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/logra.h"
 #include "launch.hpp"
 #include "signs.hpp"
@@ -64,6 +66,39 @@ bool read_opts(const logra_launch_opts *o, Opts *out) {
 }
 
 }  // namespace
+
+// Scratch of logra_update_sqnorm_noalloc, for callers that cannot allocate:
+// every device the library runs on holds its own copy until the process
+// ends, and every call on that device shares it. In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address
+// comes from hipGetSymbolAddress, once per device, and is kept in
+// scratch_addr (a cache of a fixed address, written at most once per device
+// with the value every caller would write).
+constexpr size_t kNoallocScratchBytes = LOGRA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void *> scratch_addr[kMaxDevices];
+
+// The device address of this device's scratch, or null (with the HIP error
+// in *err) if the current device cannot be queried.
+static void *device_scratch(hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+        if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    scratch_addr[dev].store(p, std::memory_order_release);
+    return p;
+}
 
 extern "C" {
 
@@ -293,6 +328,22 @@ static logra_status update_sqnorm_parts(const logra_matrix *m, int compute_dtype
     a.partials = static_cast<float *>(ws);
     if (launch_apply_f32(0, a, st) != hipSuccess) return LOGRA_ERR_HIP;
     return from_hip(launch_sqnorm_final(a.partials, apply_blocks_f32(m->d), sqnorm, st));
+}
+
+logra_status logra_update_sqnorm_noalloc(const logra_matrix *m, int compute_dtype, const float *S,
+                                         const float *v, float beta2, float eps, float *v_new,
+                                         float *rowsq, float *sqnorm, void *stream) {
+    // the same validation as logra_update_sqnorm, before the scratch is touched
+    logra_status stt = check_apply_common(m, compute_dtype, S, beta2, eps);
+    if (stt != LOGRA_OK) return stt;
+    if (!v || !v_new || !sqnorm || v_new == v) return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = sqnorm_ws_bytes(m, compute_dtype);
+    if (need > kNoallocScratchBytes) return LOGRA_ERR_WORKSPACE;
+    hipError_t e = hipSuccess;
+    void *ws = device_scratch(&e);
+    if (!ws) return LOGRA_ERR_HIP;
+    return update_sqnorm_parts(m, compute_dtype, S, v, beta2, eps, v_new, rowsq, sqnorm, ws, kNoallocScratchBytes,
+                               stream, kSqnormGram | kSqnormRows);
 }
 
 // Workspace slice of matrix i of a batch: the single-matrix layout, each

@@ -55,9 +55,38 @@ def test_no_process_wide_settings(lib):
     for f in sorted(os.listdir(src)):
         for line in open(os.path.join(src, f)):
             # a static declaration that is neither a function nor a constant
-            # is mutable state shared by every call
+            # is mutable state shared by every call; the one exception is the
+            # device scratch of the allocation-free pass 1 and the per-device
+            # cache of its (fixed) address
             if line.startswith("static ") and "(" not in line.split("=")[0]:
+                if f == "api.hip" and re.match(r"static (__device__ __align__\(256\) unsigned char scratch|"
+                                               r"std::atomic<void \*> scratch_addr)\[", line):
+                    continue
                 assert line.startswith(("static constexpr", "static const ")), (f, line)
+
+
+def test_noalloc_pass1_validation_before_any_device_call(lib):
+    # above the scratch limit: WORKSPACE; bad arguments: INVALID_ARGUMENT or
+    # UNSUPPORTED; all answered before the device is touched
+    from rank_gradient_sketching_sketch_amd import binding as B
+    r = ctypes.byref
+    V2 = ctypes.c_void_p(0x20000)
+    big = B.MatrixDesc(6287360 + 16, 64, 256, 0, 0, 0)
+    assert B.logra_sqnorm_workspace_bytes(big, B.LOGRA_BF16) > B.NOALLOC_SCRATCH_BYTES
+    ok = B.MatrixDesc(6287360, 64, 256, 0, 0, 0)
+    assert B.logra_sqnorm_workspace_bytes(ok, B.LOGRA_BF16) <= B.NOALLOC_SCRATCH_BYTES
+
+    def call(mm, compute=1, beta2=0.9, eps=1e-8, v_new=V2, sqn=FAKE):
+        return lib.logra_update_sqnorm_noalloc(r(mm), compute, FAKE, FAKE, ctypes.c_float(beta2),
+                                               ctypes.c_float(eps), v_new, None, sqn, None)
+    assert call(big) == 3
+    assert call(B.MatrixDesc(1048576 + 8, 64, 256, 0, 0, 0), compute=0) == 3
+    assert call(ok, beta2=1.5) == 1
+    assert call(ok, v_new=FAKE) == 1          # v' must not alias v
+    assert call(ok, sqn=None) == 1
+    assert call(B.MatrixDesc(64, 64, 48, 0, 0, 0)) == 2
+    assert lib.logra_update_sqnorm_noalloc(None, 1, FAKE, FAKE, ctypes.c_float(0.9), ctypes.c_float(1e-8),
+                                           V2, None, FAKE, None) == 1
 
 
 def test_launch_opts_validation(lib):
