@@ -44,6 +44,7 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # Sources that define the fold kernel: its HBM counters are reported only
 # while these are unchanged since the counters were taken.
 FOLD_SOURCES = ("rank_gradient_sketching_sketch_amd/csrc/fold_bf16.hip",
+                "rank_gradient_sketching_sketch_amd/csrc/fold_body.hpp",
                 "rank_gradient_sketching_sketch_amd/csrc/common.hpp",
                 "rank_gradient_sketching_sketch_amd/csrc/launch.hpp")
 # Predicted-KL controller run on every step's sqnorms and reported: an

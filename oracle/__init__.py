@@ -67,6 +67,8 @@ def _load():
     lib.oracle_sketch_rows.argtypes = [i64, i64, P, i64, P, i64, P, P, ctypes.c_int]
     lib.oracle_reconstruct_rows.restype = None
     lib.oracle_reconstruct_rows.argtypes = [i64, i64, i64, P, P, P]
+    lib.oracle_backward_dx_rows.restype = None
+    lib.oracle_backward_dx_rows.argtypes = [i64, i64, P, i64, P, i64, i64, P, P]
     lib.oracle_rowadam_rows.restype = dbl
     lib.oracle_rowadam_rows.argtypes = [i64, i64, i64, P, P, P, dbl, dbl, dbl, dbl,
                                         P, P, P, P, P]
@@ -197,6 +199,28 @@ def reconstruct_rows(S_rows, A) -> np.ndarray:
     G = np.zeros((nrows, k), dtype=np.float64)
     _load().oracle_reconstruct_rows(k, r, nrows, _ptr(S_rows), _ptr(A), _ptr(G))
     return G
+
+
+# ----------------------------------------------------------- backward dX ---
+
+def backward_dx_rows(dY, W, rows=None) -> np.ndarray:
+    """dX[rows] = dY[rows] W: the input gradient of Y = X W^T for the listed
+    token rows (all when rows is None). dY is T x d, W is d x k."""
+    dY = _f64(dY)
+    W = _f64(W)
+    T, d = dY.shape
+    assert W.shape[0] == d
+    k = W.shape[1]
+    if rows is None:
+        nrows, rows_arr = T, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.shape[0]
+        assert nrows == 0 or (rows_arr.min() >= 0 and rows_arr.max() < T)
+    out = np.zeros((nrows, k), dtype=np.float64)
+    _load().oracle_backward_dx_rows(d, k, _ptr(dY), d, _ptr(W), k, nrows,
+                                    None if rows_arr is None else _ptr(rows_arr), _ptr(out))
+    return out
 
 
 # --------------------------------------------------------------- RowAdam ---

@@ -31,6 +31,8 @@
  *   sqnorm   = sum_ij (Ghat_ij u_i)^2, the quantity a step controller
  *                                  reads before the update       [DAIR]
  *   W'_ij    = W_ij - lr * scale * Ghat_ij * u_i
+ *   dX       = dY W               (T x k), the backward input gradient
+ *                                  computed from the same dY     [NEWS]
  *
  * Readings where the pages leave a step open (each is listed in the design
  * notes): the hash is SplitMix64 (Steele, Lea & Flood, OOPSLA 2014) keyed as
@@ -243,4 +245,28 @@ double oracle_rowadam_rows(int64_t k, int64_t r, int64_t nrows,
     for (int64_t q = 0; q < nrows; ++q) total += tmp_sq[q];
     free(tmp_sq);
     return total;
+}
+
+/* ------------------------------------------------------- backward dX --- */
+
+/* dX rows = dY rows W: the input gradient of the sketched projection
+ * Y = X W^T, dX[t][j] = sum_i dY[t][i] W[i][j], for the listed token rows
+ * (rows == NULL: 0..nrows-1). dY is T x d (row stride lddy), W is d x k
+ * (row stride ldw), dX_rows is nrows x k. The backward pass computes it
+ * from the same dY that the sketch accumulates into S during
+ * backpropagation [NEWS "Why it matters"]. */
+void oracle_backward_dx_rows(int64_t d, int64_t k, const double *dY, int64_t lddy,
+                             const double *W, int64_t ldw, int64_t nrows,
+                             const int64_t *rows, double *dX_rows) {
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < nrows; ++q) {
+        int64_t t = rows ? rows[q] : q;
+        double *out = dX_rows + q * k;
+        for (int64_t j = 0; j < k; ++j) out[j] = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            double g = dY[t * lddy + i];
+            for (int64_t j = 0; j < k; ++j)
+                out[j] += g * W[i * ldw + j];
+        }
+    }
 }
