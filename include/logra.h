@@ -123,7 +123,13 @@ typedef struct logra_matrix {
  *                       negative value makes every such workgroup give up
  *                       without polling, which forces that path from the
  *                       host (for tests of it).
- *   reserved            must be 0 (INVALID_ARGUMENT otherwise).
+ *   backward_fold       where logra_backward_dx_sketch runs the fold: 0 =
+ *                       the library's choice (in the product's launch when
+ *                       it is expected to finish within the product, else
+ *                       after it), 1 = in the product's launch, 2 = as the
+ *                       sketch's fold kernel after the product. Results are
+ *                       the same either way to the oracle's tolerance (dX is
+ *                       bit-identical). Other values: INVALID_ARGUMENT.
  *   fold_timeouts       DEVICE pointer to one int32, or NULL. Every fold
  *                       workgroup that gives up adds 1 to it (a device-scope
  *                       atomic add), so a caller can tell a time-out from
@@ -134,7 +140,7 @@ typedef struct logra_launch_opts {
     int32_t sketch_concurrency;
     int32_t apply_concurrency;
     int32_t fold_wait_limit;
-    int32_t reserved;
+    int32_t backward_fold;
     int32_t *fold_timeouts;
 } logra_launch_opts;
 
@@ -229,6 +235,61 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
                                float *S, int accumulate,
                                void *ws, size_t ws_bytes,
                                const logra_launch_opts *opts, void *stream);
+
+/*
+ * logra_backward_dx -- the backward input gradient of the projection,
+ *        dX = dY W        (T x k; W is d x k, the layer computes Y = X W^T),
+ * bf16 inputs and output, fp32 accumulation, rounded to bf16 (nearest even).
+ * Not an operation of the sketch itself: the product the backward pass
+ * computes from the same dY that the sketch accumulates "during
+ * backpropagation" ("NVIDIA's LoGRA fits RL post-training...", section "Why
+ * it matters"), provided here as the yardstick for, and the product half of,
+ * logra_backward_dx_sketch.
+ * Arguments:
+ *   m        d, k of W (r, seed, step and id are not used here).
+ *   T        tokens (rows of dY and dX), >= 0; T == 0 launches nothing.
+ *   act_dtype LOGRA_BF16 (the only one supported).
+ *   dY       T x d, row stride lddy >= d.    W: d x k, row stride ldw >= k.
+ *   dX       T x k, row stride lddx >= k, out (written only).
+ *   opts     launch options (none is read by the product), or NULL.
+ * Requirements: d, k, lddy, ldw, lddx multiples of 8; dY, W, dX 16-byte
+ *   aligned; each of dY, W, dX below 2^31 bytes.
+ * Errors: INVALID_ARGUMENT (nulls, T < 0, ld < cols, misalignment, bad
+ *   opts), UNSUPPORTED (dtype, shapes above), HIP.
+ */
+logra_status logra_backward_dx(const logra_matrix *m, int64_t T, int act_dtype,
+                               const void *dY, int64_t lddy, const void *W, int64_t ldw,
+                               void *dX, int64_t lddx, const logra_launch_opts *opts, void *stream);
+
+/*
+ * logra_backward_dx_sketch -- logra_backward_dx and logra_sketch_fold in one
+ * launch: dX = dY W and S (+)= dY^T (X A^T), the sketch accumulated during
+ * backpropagation next to the input gradient computed from the same dY
+ * ("NVIDIA's LoGRA fits RL post-training...", section "Why it matters":
+ * S = G A^T accumulated during backpropagation). Most workgroups compute dX
+ * on the matrix cores; a few run the fold on the compute units and memory
+ * bandwidth the product leaves free. Where the fold would outlast the
+ * product beside it (small d: few fold tiles, each over all tokens), the
+ * call runs the product and then the sketch's fold kernel instead, one after
+ * the other on the stream. dX is bit-identical to logra_backward_dx; S
+ * matches logra_sketch_fold to the same tolerance of the oracle (in the one
+ * launch its tiles cover all tokens, so its summation order differs).
+ * Arguments: as logra_backward_dx, plus
+ *   m        the full matrix descriptor (r, seed, step, id of this step).
+ *   S        d x r fp32, in/out; accumulate as in logra_sketch_fold.
+ *   ws       the sketch workspace holding the projection X A^T of this
+ *            microbatch made by logra_sketch_project (the same m, T and
+ *            act_dtype); only the projection is read.
+ *   opts     launch options (fold_wait_limit and fold_timeouts apply when
+ *            the fold runs as its own kernel), or NULL.
+ * Requirements and errors: those of logra_backward_dx and logra_sketch_fold
+ *   together. T == 0 leaves S unchanged (accumulate != 0) or zeroes it.
+ */
+logra_status logra_backward_dx_sketch(const logra_matrix *m, int64_t T, int act_dtype,
+                                      const void *dY, int64_t lddy, const void *W, int64_t ldw,
+                                      void *dX, int64_t lddx, float *S, int accumulate,
+                                      void *ws, size_t ws_bytes,
+                                      const logra_launch_opts *opts, void *stream);
 
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs

@@ -11,6 +11,7 @@ __all__ = [
     "logra_abi_version", "logra_status_string", "logra_sign_words",
     "logra_sketch_workspace_bytes", "logra_sketch_accumulate",
     "logra_sketch_project", "logra_sketch_fold", "LaunchOpts",
+    "logra_backward_dx", "logra_backward_dx_sketch",
     "logra_sqnorm_workspace_bytes", "logra_update_sqnorm", "logra_rowadam_apply",
     "logra_sqnorm_prepare", "logra_update_sqnorm_prepared", "logra_update_sqnorm_noalloc",
     "logra_sqnorm_batch_workspace_bytes", "logra_update_sqnorm_batch",

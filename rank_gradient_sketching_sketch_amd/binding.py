@@ -40,16 +40,16 @@ class MatrixDesc(ctypes.Structure):
 
 
 class LaunchOpts(ctypes.Structure):
-    """logra_launch_opts: per-call scheduling hints and the fold's wait
-    guard (0 = default for each field). fold_timeouts may be given as an
+    """logra_launch_opts: per-call scheduling hints, the fold's wait guard and
+    where the backward call runs its fold (0 = default for each field). fold_timeouts may be given as an
     int32 device tensor of one element (or a raw device address); every fold
     workgroup that gives up on its partner adds 1 to it."""
     _fields_ = [("sketch_concurrency", ctypes.c_int32), ("apply_concurrency", ctypes.c_int32),
-                ("fold_wait_limit", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("fold_wait_limit", ctypes.c_int32), ("backward_fold", ctypes.c_int32),
                 ("fold_timeouts", ctypes.c_void_p)]
 
     def __init__(self, sketch_concurrency=0, apply_concurrency=0, fold_wait_limit=0,
-                 fold_timeouts=None):
+                 fold_timeouts=None, backward_fold=0):
         addr = None
         if fold_timeouts is not None:
             if isinstance(fold_timeouts, torch.Tensor):
@@ -58,7 +58,8 @@ class LaunchOpts(ctypes.Structure):
                 addr = fold_timeouts.data_ptr()
             else:
                 addr = int(fold_timeouts)
-        super().__init__(int(sketch_concurrency), int(apply_concurrency), int(fold_wait_limit), 0, addr)
+        super().__init__(int(sketch_concurrency), int(apply_concurrency), int(fold_wait_limit),
+                         int(backward_fold), addr)
 
 
 class KLBudget(ctypes.Structure):
@@ -103,6 +104,10 @@ def load_library():
     lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, O, P]
     lib.logra_sketch_fold.restype = i32
     lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, O, P]
+    lib.logra_backward_dx.restype = i32
+    lib.logra_backward_dx.argtypes = [D, i64, i32, P, i64, P, i64, P, i64, O, P]
+    lib.logra_backward_dx_sketch.restype = i32
+    lib.logra_backward_dx_sketch.argtypes = [D, i64, i32, P, i64, P, i64, P, i64, P, i32, P, sz, O, P]
     lib.logra_sqnorm_workspace_bytes.restype = sz
     lib.logra_sqnorm_workspace_bytes.argtypes = [D, i32]
     lib.logra_update_sqnorm.restype = i32
@@ -217,6 +222,25 @@ def logra_sketch_fold(m: MatrixDesc, dY: torch.Tensor, S: torch.Tensor, accumula
     _check(load_library().logra_sketch_fold(
         ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(S),
         1 if accumulate else 0, _ptr(ws), nb, _opts(opts), _stream(stream)), "logra_sketch_fold")
+
+
+def logra_backward_dx(m: MatrixDesc, dY: torch.Tensor, W: torch.Tensor, dX: torch.Tensor, stream=None,
+                      opts: Optional[LaunchOpts] = None) -> None:
+    """dX = dY W (bf16): the backward input gradient of Y = X W^T."""
+    _check(load_library().logra_backward_dx(
+        ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(W), _ld(W), _ptr(dX), _ld(dX),
+        _opts(opts), _stream(stream)), "logra_backward_dx")
+
+
+def logra_backward_dx_sketch(m: MatrixDesc, dY: torch.Tensor, W: torch.Tensor, dX: torch.Tensor,
+                             S: torch.Tensor, accumulate: bool, ws: torch.Tensor, stream=None,
+                             opts: Optional[LaunchOpts] = None) -> None:
+    """dX = dY W and S (+)= dY^T (X A^T) in one launch, the projection read
+    from ws (left there by logra_sketch_project)."""
+    _check(load_library().logra_backward_dx_sketch(
+        ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(W), _ld(W), _ptr(dX), _ld(dX),
+        _ptr(S), 1 if accumulate else 0, _ptr(ws), ws.numel() * ws.element_size(), _opts(opts),
+        _stream(stream)), "logra_backward_dx_sketch")
 
 
 def logra_sqnorm_workspace_bytes(m: MatrixDesc, compute_dtype: int) -> int:

@@ -47,13 +47,15 @@ bool fits_view(int64_t rows, int64_t ld, int64_t elem) { return rows * ld * elem
 struct Opts {
     int sketch_concurrency = 1;
     int apply_concurrency = 1;
+    int backward_fold = 0;
     FoldWait wait;
 };
 
 bool read_opts(const logra_launch_opts *o, Opts *out) {
     Opts r;
     if (o) {
-        if (o->reserved != 0) return false;
+        if (o->backward_fold < 0 || o->backward_fold > 2) return false;
+        r.backward_fold = o->backward_fold;
         if (o->sketch_concurrency < 0 || o->sketch_concurrency > 256) return false;
         if (o->apply_concurrency < 0 || o->apply_concurrency > 256) return false;
         if (o->sketch_concurrency > 0) r.sketch_concurrency = o->sketch_concurrency;
@@ -235,6 +237,62 @@ logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_d
     hipError_t h = do_project(m, T, act_dtype, X, ldx, ws, o, st);
     if (h != hipSuccess) return LOGRA_ERR_HIP;
     return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, o, st));
+}
+
+// Arguments of the backward product shared by both entry points.
+static logra_status check_dx(const logra_matrix *m, int64_t T, int act_dtype, const void *dY, int64_t lddy,
+                             const void *W, int64_t ldw, const void *dX, int64_t lddx) {
+    if (!matrix_ok(m) || T < 0) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (act_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
+    if (m->d % 8 || m->k % 8 || T > (1ll << 30)) return LOGRA_ERR_UNSUPPORTED;
+    if (!W || ldw < m->k || ldw % 8 || !aligned16(W)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!fits_view(m->d, ldw, 2)) return LOGRA_ERR_UNSUPPORTED;
+    if (T == 0) return LOGRA_OK;
+    if (!dY || lddy < m->d || lddy % 8 || !aligned16(dY)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!dX || lddx < m->k || lddx % 8 || !aligned16(dX)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!fits_view(T, lddy, 2) || !fits_view(T, lddx, 2)) return LOGRA_ERR_UNSUPPORTED;
+    return LOGRA_OK;
+}
+
+logra_status logra_backward_dx(const logra_matrix *m, int64_t T, int act_dtype, const void *dY, int64_t lddy,
+                               const void *W, int64_t ldw, void *dX, int64_t lddx,
+                               const logra_launch_opts *opts, void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
+    const logra_status e = check_dx(m, T, act_dtype, dY, lddy, W, ldw, dX, lddx);
+    if (e != LOGRA_OK || T == 0) return e;
+    // the r = 256 instance of the launch, the one the fused call runs at the
+    // 7B shapes, so the two time the same product code
+    return from_hip(launch_dx_bf16(256, T, m->d, m->k, static_cast<const uint16_t *>(dY), lddy,
+                                   static_cast<const uint16_t *>(W), ldw, static_cast<uint16_t *>(dX), lddx,
+                                   nullptr, 0, nullptr, 0, 0, o.wait, static_cast<hipStream_t>(stream)));
+}
+
+logra_status logra_backward_dx_sketch(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
+                                      int64_t lddy, const void *W, int64_t ldw, void *dX, int64_t lddx,
+                                      float *S, int accumulate, void *ws, size_t ws_bytes,
+                                      const logra_launch_opts *opts, void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
+    logra_status e = check_dx(m, T, act_dtype, dY, lddy, W, ldw, dX, lddx);
+    if (e == LOGRA_OK) e = check_sketch(m, T, act_dtype);
+    if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
+    if (e != LOGRA_OK) return e;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) return accumulate ? LOGRA_OK : from_hip(launch_fill_zero(S, m->d * m->r, st));
+    const int r = static_cast<int>(m->r);
+    const Stage1Plan p = plan_stage1_bf16(T, m->k, r);
+    const uint16_t *dy = static_cast<const uint16_t *>(dY);
+    const bool fuse = o.backward_fold == 1 || (o.backward_fold == 0 && dx_fuse_pays(T, m->d, m->k, r));
+    if (fuse)
+        return from_hip(launch_dx_bf16(r, T, m->d, m->k, dy, lddy, static_cast<const uint16_t *>(W), ldw,
+                                       static_cast<uint16_t *>(dX), lddx, static_cast<const uint16_t *>(ws),
+                                       p.t_blocks, S, accumulate ? 1 : 0, 1, o.wait, st));
+    // the fold would outlast the product beside it: the product, then the fold
+    if (launch_dx_bf16(r, T, m->d, m->k, dy, lddy, static_cast<const uint16_t *>(W), ldw,
+                       static_cast<uint16_t *>(dX), lddx, nullptr, 0, nullptr, 0, 0, o.wait, st) != hipSuccess)
+        return LOGRA_ERR_HIP;
+    return from_hip(launch_fold_bf16(r, T, m->d, m->k, dy, lddy, S, accumulate ? 1 : 0, ws, o.wait, st));
 }
 
 size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype) {

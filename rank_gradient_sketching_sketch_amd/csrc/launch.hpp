@@ -45,6 +45,22 @@ struct FoldWait {
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, const FoldWait &wait, hipStream_t st);
+// The backward input gradient dX = dY W (bf16, 256 x 256 product tiles)
+// and, when sketch != 0, the fold S (+)= dY^T P in the same launch (P read
+// from the projection the sketch workspace holds).
+struct DxPlan {
+    int n_tm = 0, n_tn = 0;       // product tiles
+    int n_fold = 0;               // fold workgroups
+    int fold_nblk = 0, fold_tiles = 0;
+};
+DxPlan plan_dx_bf16(int64_t T, int64_t D, int64_t K, int sketch);
+// Whether running the fold beside the product in one launch is expected to
+// be faster than the product and then the sketch's fold kernel.
+bool dx_fuse_pays(int64_t T, int64_t D, int64_t K, int R);
+hipError_t launch_dx_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
+                          const uint16_t *W, int64_t ldw, uint16_t *dX, int64_t lddx, const uint16_t *P,
+                          int p_blocks, float *S, int accumulate, int sketch, const FoldWait &wait,
+                          hipStream_t st);
 size_t workspace_sketch_f32(int64_t T, int64_t R);
 int apply_blocks_f32(int64_t D);
 

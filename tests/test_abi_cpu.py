@@ -90,8 +90,8 @@ def test_noalloc_pass1_validation_before_any_device_call(lib):
 
 
 def test_launch_opts_validation(lib):
-    # out-of-range hints and a non-zero reserved field are refused before any
-    # launch; NULL and a zeroed struct are the defaults
+    # out-of-range hints and fold placements are refused before any launch;
+    # NULL and a zeroed struct are the defaults
     from rank_gradient_sketching_sketch_amd import binding as B
     m = _m()
     r = ctypes.byref
@@ -109,17 +109,18 @@ def test_launch_opts_validation(lib):
     assert acc(bad_opts(sketch_concurrency=-1)) == 1
     assert acc(bad_opts(sketch_concurrency=257)) == 1
     assert acc(bad_opts(apply_concurrency=300)) == 1
-    assert acc(bad_opts(reserved=1)) == 1
-    assert lib.logra_sketch_project(r(m), T, 1, FAKE, 128, FAKE, ws, bad_opts(reserved=2), None) == 1
+    assert acc(bad_opts(backward_fold=3)) == 1
+    assert acc(bad_opts(backward_fold=-1)) == 1
+    assert lib.logra_sketch_project(r(m), T, 1, FAKE, 128, FAKE, ws, bad_opts(backward_fold=7), None) == 1
     assert lib.logra_sketch_fold(r(m), T, 1, FAKE, 64, FAKE, 0, FAKE, ws, bad_opts(sketch_concurrency=-5),
                                  None) == 1
     assert lib.logra_rowadam_apply(r(m), 1, FAKE, FAKE, FAKE, 1, 128, ctypes.c_float(1e-3), ctypes.c_float(1.0),
                                    ctypes.c_float(1e-8), bad_opts(apply_concurrency=-1), None) == 1
     # the option checks come first: a bad option with T == 0 (no launch) is still refused
     assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0,
-                                       bad_opts(reserved=7), None) == 1
+                                       bad_opts(backward_fold=9), None) == 1
     # valid options with nothing to launch: accepted
-    o = B.LaunchOpts(sketch_concurrency=4, apply_concurrency=3, fold_wait_limit=-1)
+    o = B.LaunchOpts(sketch_concurrency=4, apply_concurrency=3, fold_wait_limit=-1, backward_fold=2)
     assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, r(o), None) == 0
     assert lib.logra_sketch_accumulate(r(m), 0, 1, None, 0, None, 0, FAKE, 1, None, 0, None, None) == 0
 
