@@ -45,8 +45,7 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # while these are unchanged since the counters were taken.
 FOLD_SOURCES = ("rank_gradient_sketching_sketch_amd/csrc/fold_bf16.hip",
                 "rank_gradient_sketching_sketch_amd/csrc/fold_body.hpp",
-                "rank_gradient_sketching_sketch_amd/csrc/common.hpp",
-                "rank_gradient_sketching_sketch_amd/csrc/launch.hpp")
+                "rank_gradient_sketching_sketch_amd/csrc/common.hpp")
 # Predicted-KL controller run on every step's sqnorms and reported: an
 # isotropic Fisher of scale 1 and a budget annealed from 1e-3 to 1e-4 nats
 # over 1000 steps (the pages give no values). The update itself uses the
@@ -127,6 +126,8 @@ def parse():
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward dX product (alone and with the fold beside it)")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time torch.mm (the vendor GEMM) on the fold's contraction and on the "
                          "dense dY^T X it replaces, for context")
@@ -364,6 +365,10 @@ def main():
                        "applied": False},
     }
 
+    if code == B.LOGRA_BF16 and not args.no_backward:
+        spec = wl.matrices[big]
+        result["backward_dx"] = backward_dx(wl, spec, mats[big].W, xbuf[xkey(spec, 0, 0)],
+                                            [ybuf[ykey(spec, 0, mb)] for mb in range(min(nmb, 3))], fold_ms)
     if args.yardstick:
         result["yardstick"] = yardstick(wl, fold_ms if len(mats) == 1 else None)
     if not args.no_cpu_baseline:
@@ -374,6 +379,76 @@ def main():
     if timeouts:
         print("fold time-outs: %d workgroups gave up waiting for their partner" % timeouts, file=sys.stderr)
         sys.exit(3)
+
+
+def backward_dx(wl, spec, W, X, dYs, fold_ms, reps=15):
+    """The backward input gradient dX = dY W of the largest matrix at the
+    workload's token count: the library's product alone
+    (logra_backward_dx) and the product with the sketch's fold beside it
+    (logra_backward_dx_sketch), timed in alternation, one event pair per call
+    (the projection made beforehand, as in the sketch step), medians; and
+    torch.mm on the same operands for context."""
+    import statistics
+    import torch
+    from rank_gradient_sketching_sketch_amd import binding as B
+    T, d, k, r = wl.tokens, spec.d, spec.k, wl.r
+    dev = W.device
+    m = B.MatrixDesc(d, k, r, seed=0, step=0, matrix_id=spec.matrix_id)
+    ws = torch.empty(B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+    S = torch.zeros(d, r, dtype=torch.float32, device=dev)
+    dX = torch.empty(T, k, dtype=torch.bfloat16, device=dev)
+    B.logra_sketch_project(m, X, ws)
+    auto = B.LaunchOpts()
+
+    def timed(fn, i):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    runs = {"product": lambda i: B.logra_backward_dx(m, dYs[i % len(dYs)], W, dX),
+            "fused": lambda i: B.logra_backward_dx_sketch(m, dYs[i % len(dYs)], W, dX, S, True, ws, opts=auto),
+            "torch_mm": lambda i: torch.mm(dYs[i % len(dYs)], W)}
+    for name, fn in runs.items():
+        for i in range(3):
+            fn(i)
+    torch.cuda.synchronize()
+    t = {name: [] for name in runs}
+    for i in range(reps):
+        for name, fn in runs.items():
+            t[name].append(timed(fn, i))
+    med = {name: statistics.median(v) for name, v in t.items()}
+    flop = 2.0 * T * d * k
+    out = {"shape_Tdk": [T, d, k], "r": r,
+           "product_us": round(med["product"], 2),
+           "product_tflops": round(flop / med["product"] / 1e6, 1),
+           "product_frac_bf16_peak": round(flop / med["product"] / 1e6 / PEAK_BF16_TFLOPS, 4),
+           "fused_us": round(med["fused"], 2),
+           "sketch_incremental_us": round(med["fused"] - med["product"], 2),
+           "fold_in_step_us": round(fold_ms * 1e3, 2),
+           "placement": "in the product's launch" if _fuses(m, T) else "after the product",
+           "torch_mm_us": round(med["torch_mm"], 2),
+           "torch_mm_tflops": round(flop / med["torch_mm"] / 1e6, 1),
+           "timing": "medians of %d alternating calls, one event pair each" % reps}
+    del ws, S, dX
+    torch.cuda.empty_cache()
+    return out
+
+
+def _fuses(m, T):
+    """Whether logra_backward_dx_sketch runs the fold in the product's launch
+    for this shape (the planner's rule, mirrored for the report: the fold
+    workgroups' share of all-token tiles against three quarters of the
+    product at 700 TFLOP/s, 60 GB/s per fold workgroup)."""
+    G = -(-T // 256) * -(-m.k // 256)
+    tiles = -(-(-(-m.d // 16)) // 10)
+    spare = 0 if G % 256 == 0 else 256 - G % 256
+    n_fold = min(max(spare, 32), tiles)
+    per_wg = -(-tiles // n_fold) * 2.0 * T * (160 + m.r) / 60e9
+    return per_wg <= 0.75 * (2.0 * T * m.d * m.k / 700e12)
 
 
 def yardstick(wl, fold_ms):

@@ -48,3 +48,21 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_fold_bytes_per_launch():
+    T, d, r = 4096, 18944, 256
+    assert bench.fold_bytes_per_launch(T, d, r, True) == 196083712
+    assert bench.fold_bytes_per_launch(T, d, r, False) == 196083712 - 4 * d * r
+
+
+def test_traffic_record_is_tied_to_the_fold_sources(monkeypatch):
+    rec = bench.fold_traffic_record("qwen7b_up")
+    # the committed record parses and carries counter bytes per dispatch
+    # (None only if the fold sources changed after the counters were taken)
+    if rec is not None:
+        assert rec["fold_bytes_per_dispatch"] > bench.fold_bytes_per_launch(4096, 18944, 256, True)
+        assert rec["fold_sources_sha256"] == bench.fold_sources_sha256()
+    monkeypatch.setattr(bench, "fold_sources_sha256", lambda: "0" * 64)
+    assert bench.fold_traffic_record("qwen7b_up") is None
+    assert bench.fold_traffic_record("no_such_workload") is None
