@@ -95,22 +95,24 @@ def fold_sources_sha256():
     return h.hexdigest()
 
 
-def fold_traffic_record(workload):
+def fold_traffic_record(workload, call="logra_sketch_fold_parts"):
     """The fold's HBM bytes per dispatch from the committed counter summary
-    (profiles/hbm_traffic_<workload>.md, a JSON line after 'traffic-record:'),
-    or None when there is none or it was taken on other fold sources."""
+    (profiles/hbm_traffic_<workload>.md, JSON lines after 'traffic-record:',
+    one per fold call), for the call the bench timed; None when there is
+    none or it was taken on other fold sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
     try:
         text = open(path).read()
     except OSError:
         return None
-    m = re.search(r"traffic-record:\s*(\{.*\})", text)
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
-    if rec.get("fold_sources_sha256") != fold_sources_sha256():
-        return None
-    return rec
+    for m in re.finditer(r"traffic-record:\s*(\{.*\})", text):
+        rec = json.loads(m.group(1))
+        if rec.get("call", "logra_sketch_fold") != call:
+            continue
+        if rec.get("fold_sources_sha256") != fold_sources_sha256():
+            return None
+        return rec
+    return None
 
 
 def parse():
@@ -124,6 +126,8 @@ def parse():
                     help="streams the matrices' sketch calls are spread over (0: at most 4)")
     ap.add_argument("--apply-streams", type=int, default=0,
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
+    ap.add_argument("--parts", default="pair", choices=("pair", "all", "none"),
+                    help="which matrices keep their sketch in parts during the step (logra_sketch_fold_parts)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
     ap.add_argument("--no-backward", action="store_true",
@@ -198,7 +202,7 @@ def main():
                    v=inputs.second_moment(wl, s, device=dev), name="%s.%d" % (s.name, s.layer))
             for s in wl.matrices]
     step_runner = Step(mats, r, T, code, device=dev, sketch_lanes=args.streams,
-                       apply_lanes=args.apply_streams, batch_pass1=not args.no_batch)
+                       apply_lanes=args.apply_streams, batch_pass1=not args.no_batch, parts=args.parts)
 
     # Microbatch buffers. One-matrix workloads: fresh X and dY for every
     # step and microbatch (as many step sets as the input budget holds,
@@ -305,7 +309,8 @@ def main():
     spec_big = wl.matrices[big]
     fold_bytes = fold_bytes_per_launch(T, spec_big.d, r, probe_mb > 0)
     fold_gbps = fold_bytes / (fold_ms * 1e-3) / 1e9
-    rec = fold_traffic_record(wl.name)
+    probed_call = "logra_sketch_fold_parts" if mats[big].parts is not None else "logra_sketch_fold"
+    rec = fold_traffic_record(wl.name, probed_call)
     traffic = None if rec is None else int(round(rec["fold_bytes_per_dispatch"]))
     dev_free, dev_total = torch.cuda.mem_get_info(dev)
 
@@ -337,7 +342,9 @@ def main():
                   "ms_per_step": round(apply_ms, 4),
                   "sqnorm_ms": round(tot["sqnorm"] / K, 5), "rowadam_ms": round(tot["apply"] / K, 5),
                   "skipped_nonfinite": skipped[0]},
-        "roofline": {"kernel": "fold_bf16_kernel (logra_sketch_fold)", "bound": "hbm",
+        "roofline": {"kernel": ("fold_bf16_kernel (logra_sketch_fold_parts, a middle microbatch)"
+                                if mats[big].parts is not None else "fold_bf16_kernel (logra_sketch_fold)"),
+                     "bound": "hbm",
                      "achieved": round(fold_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(fold_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
@@ -355,7 +362,8 @@ def main():
                    "weights": sum(m.W.numel() * m.W.element_size() for m in mats),
                    "microbatch_inputs": sum(t.numel() * t.element_size()
                                             for t in list(xbuf.values()) + list(ybuf.values())),
-                   "workspaces": step_runner.workspace_bytes},
+                   "workspaces": step_runner.workspace_bytes,
+                   "sketch_parts": step_runner.parts_bytes},
         "streams": {"sketch": step_runner.n_sketch, "apply": step_runner.n_apply,
                     "pass1_batches": sum(1 for b in step_runner.batches if b[2] is not None)},
         "controller": {"fisher_scale": KL_PHI,

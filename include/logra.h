@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LOGRA_ABI_VERSION 3
+#define LOGRA_ABI_VERSION 4
 
 typedef enum logra_status {
     LOGRA_OK = 0,
@@ -235,6 +235,54 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype,
                                float *S, int accumulate,
                                void *ws, size_t ws_bytes,
                                const logra_launch_opts *opts, void *stream);
+
+/*
+ * logra_sketch_parts_bytes / logra_sketch_fold_parts -- the fold with the
+ * step's sketch kept in parts while its microbatches arrive, so that the
+ * workgroups sharing a tile of S neither exchange partial tiles nor wait for
+ * each other (the sketch is the same S = G A^T summed over the step's
+ * microbatches: "NVIDIA's LoGRA fits RL post-training...", section "Why it
+ * matters"; "LoGRA: Scaling LLM Reinforcement Learning...", paragraph
+ * "Gradient sketches."; how its sum is held during the step is this
+ * library's choice).
+ * Between the calls of a step the sketch of the microbatches folded so far
+ * is S + part_0 + ... + part_{n-2}, where the parts are n - 1 arrays of
+ * d x r fp32 in `parts` and n is the number of workgroups that share each
+ * tile of S for this (m, T, act_dtype); the call with LOGRA_FOLD_LAST adds
+ * the parts into S (in part order), after which S alone holds the sketch.
+ * logra_sketch_parts_bytes returns (n - 1) d r 4 bytes: 0 when one
+ * workgroup covers each tile (or on the fp32 path), and then fold_parts is
+ * logra_sketch_fold with accumulate = !(phase & LOGRA_FOLD_FIRST). It
+ * returns 0 for invalid arguments too.
+ * Arguments: as logra_sketch_fold, with
+ *   parts    device, parts_bytes >= logra_sketch_parts_bytes(m, T,
+ *            act_dtype), 16-byte aligned, caller-owned and kept for the
+ *            whole step (one per matrix being accumulated). May be NULL
+ *            when that size is 0. Its contents between calls are the
+ *            library's.
+ *   phase    LOGRA_FOLD_FIRST: the step's first microbatch (S and the
+ *            parts are overwritten, nothing is read from them);
+ *            LOGRA_FOLD_LAST: the step's last microbatch (the parts are
+ *            added into S after the fold); both for a one-microbatch step;
+ *            0 for every other microbatch. Other bits: INVALID_ARGUMENT.
+ * Every call of a step must use the same (m, T, act_dtype), and the step
+ * must start with a LOGRA_FOLD_FIRST call. A logra_sketch_fold or
+ * logra_backward_dx_sketch call with accumulate != 0 between them adds its
+ * microbatch to S alone, which keeps the sum right. Results are
+ * deterministic; they differ from logra_sketch_fold's in summation order
+ * only (within the same tolerance of the oracle).
+ * Errors: those of logra_sketch_fold; WORKSPACE also for parts NULL or
+ *   parts_bytes too small when the size above is not 0; INVALID_ARGUMENT
+ *   for misaligned parts or a bad phase.
+ */
+#define LOGRA_FOLD_FIRST 1
+#define LOGRA_FOLD_LAST 2
+size_t logra_sketch_parts_bytes(const logra_matrix *m, int64_t T, int act_dtype);
+logra_status logra_sketch_fold_parts(const logra_matrix *m, int64_t T, int act_dtype,
+                                     const void *dY, int64_t lddy, float *S,
+                                     float *parts, size_t parts_bytes, int phase,
+                                     void *ws, size_t ws_bytes,
+                                     const logra_launch_opts *opts, void *stream);
 
 /*
  * logra_backward_dx -- the backward input gradient of the projection,

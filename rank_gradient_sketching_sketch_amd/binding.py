@@ -104,6 +104,10 @@ def load_library():
     lib.logra_sketch_project.argtypes = [D, i64, i32, P, i64, P, sz, O, P]
     lib.logra_sketch_fold.restype = i32
     lib.logra_sketch_fold.argtypes = [D, i64, i32, P, i64, P, i32, P, sz, O, P]
+    lib.logra_sketch_parts_bytes.restype = sz
+    lib.logra_sketch_parts_bytes.argtypes = [D, i64, i32]
+    lib.logra_sketch_fold_parts.restype = i32
+    lib.logra_sketch_fold_parts.argtypes = [D, i64, i32, P, i64, P, P, sz, i32, P, sz, O, P]
     lib.logra_backward_dx.restype = i32
     lib.logra_backward_dx.argtypes = [D, i64, i32, P, i64, P, i64, P, i64, O, P]
     lib.logra_backward_dx_sketch.restype = i32
@@ -222,6 +226,26 @@ def logra_sketch_fold(m: MatrixDesc, dY: torch.Tensor, S: torch.Tensor, accumula
     _check(load_library().logra_sketch_fold(
         ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(S),
         1 if accumulate else 0, _ptr(ws), nb, _opts(opts), _stream(stream)), "logra_sketch_fold")
+
+
+LOGRA_FOLD_FIRST = 1
+LOGRA_FOLD_LAST = 2
+
+
+def logra_sketch_parts_bytes(m: MatrixDesc, T: int, act_dtype: int) -> int:
+    return int(load_library().logra_sketch_parts_bytes(ctypes.byref(m), T, act_dtype))
+
+
+def logra_sketch_fold_parts(m: MatrixDesc, dY: torch.Tensor, S: torch.Tensor, parts: Optional[torch.Tensor],
+                            phase: int, ws: torch.Tensor, stream=None, opts: Optional[LaunchOpts] = None) -> None:
+    """The fold with the step's sketch held as S plus the parts between calls;
+    phase LOGRA_FOLD_FIRST / LOGRA_FOLD_LAST / both / 0."""
+    ws, nb = _sketch_ws(m, dY.shape[0], _dtype_code(dY), dY.device, ws)
+    pb = 0 if parts is None else parts.numel() * parts.element_size()
+    _check(load_library().logra_sketch_fold_parts(
+        ctypes.byref(m), dY.shape[0], _dtype_code(dY), _ptr(dY), _ld(dY), _ptr(S),
+        None if parts is None else _ptr(parts), pb, int(phase), _ptr(ws), nb, _opts(opts), _stream(stream)),
+        "logra_sketch_fold_parts")
 
 
 def logra_backward_dx(m: MatrixDesc, dY: torch.Tensor, W: torch.Tensor, dX: torch.Tensor, stream=None,

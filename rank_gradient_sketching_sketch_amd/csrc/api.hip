@@ -223,6 +223,33 @@ logra_status logra_sketch_fold(const logra_matrix *m, int64_t T, int act_dtype, 
                             static_cast<hipStream_t>(stream)));
 }
 
+size_t logra_sketch_parts_bytes(const logra_matrix *m, int64_t T, int act_dtype) {
+    if (check_sketch(m, T, act_dtype) != LOGRA_OK || T == 0 || act_dtype != LOGRA_BF16) return 0;
+    return fold_parts_bytes_bf16(T, m->d, static_cast<int>(m->r));
+}
+
+logra_status logra_sketch_fold_parts(const logra_matrix *m, int64_t T, int act_dtype, const void *dY,
+                                     int64_t lddy, float *S, float *parts, size_t parts_bytes, int phase,
+                                     void *ws, size_t ws_bytes, const logra_launch_opts *opts,
+                                     void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (phase & ~(LOGRA_FOLD_FIRST | LOGRA_FOLD_LAST)) return LOGRA_ERR_INVALID_ARGUMENT;
+    logra_status e = check_sketch(m, T, act_dtype);
+    if (e == LOGRA_OK) e = check_fold(m, T, act_dtype, dY, lddy, S, ws, ws_bytes);
+    if (e != LOGRA_OK) return e;
+    const size_t need = logra_sketch_parts_bytes(m, T, act_dtype);
+    if (need > 0) {
+        if (!parts || parts_bytes < need) return LOGRA_ERR_WORKSPACE;
+        if (!aligned16(parts)) return LOGRA_ERR_INVALID_ARGUMENT;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int accumulate = (phase & LOGRA_FOLD_FIRST) ? 0 : 1;
+    if (need == 0) return from_hip(do_fold(m, T, act_dtype, dY, lddy, S, accumulate, ws, o, st));
+    return from_hip(launch_fold_parts_ws_bf16(static_cast<int>(m->r), T, m->d, m->k,
+                                              static_cast<const uint16_t *>(dY), lddy, S, parts, phase, ws, st));
+}
+
 logra_status logra_sketch_accumulate(const logra_matrix *m, int64_t T, int act_dtype,
                                      const void *X, int64_t ldx, const void *dY, int64_t lddy,
                                      float *S, int accumulate, void *ws, size_t ws_bytes,

@@ -59,6 +59,11 @@
 //   * More members per tile (small d, so that the grid still fills the chip)
 //     each write their whole partial tile, and fold_reduce_kernel adds them in
 //     member order.
+//   * Split mode (logra_sketch_fold_parts) keeps the sketch of a step in n
+//     parts while its microbatches arrive: member 0 of every tile adds its
+//     partial to S, member q > 0 to part q - 1, each over the whole tile, so
+//     members neither exchange nor wait; the step's last fold then adds the
+//     parts into S in part order (fold_reduce_kernel).
 #include "fold_body.hpp"
 
 namespace logra {
@@ -167,6 +172,44 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                            accumulate);
     }
     return hipGetLastError();
+}
+
+template <int R>
+static hipError_t fold_parts_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy, const uint16_t *P,
+                               int p_blocks, float *S, float *parts, int phase, hipStream_t st) {
+    const FoldPlan p = plan_fold_bf16(T, D, R);
+    const int first = phase & 1, last = phase & 2;
+    auto kernel = fold_bf16_kernel<R, 5, kFoldSingle>;
+    if (p.n_split > 1)
+        kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldSplit> : fold_bf16_kernel<R, 10, kFoldSplit>;
+    else if (p.max_blocks == 10)
+        kernel = fold_bf16_kernel<R, 10, kFoldSingle>;
+    hipLaunchKernelGGL(kernel, dim3(p.n_tiles * p.n_split), dim3(256), 0, st, dY, lddy, static_cast<int>(T),
+                       static_cast<int>(D), P, p_blocks, S, parts, 0, nullptr, first ? 0 : 1, p.nblk, p.n_tiles,
+                       p.n_split, p.steps_per, 0, nullptr);
+    if (last && p.n_split > 1) {
+        const int64_t n = D * R;
+        hipLaunchKernelGGL(fold_reduce_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st, parts, p.n_split - 1,
+                           n, S, 1);
+    }
+    return hipGetLastError();
+}
+
+size_t fold_parts_bytes_bf16(int64_t T, int64_t D, int R) {
+    const FoldPlan p = plan_fold_bf16(T, D, R);
+    return p.n_split > 1 ? static_cast<size_t>(p.n_split - 1) * D * R * 4 : 0;
+}
+
+hipError_t launch_fold_parts_bf16(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
+                                  const uint16_t *P, int p_blocks, float *S, float *parts, int phase,
+                                  hipStream_t st) {
+    switch (R) {
+    case 32: return fold_parts_r<32>(T, D, dY, lddy, P, p_blocks, S, parts, phase, st);
+    case 64: return fold_parts_r<64>(T, D, dY, lddy, P, p_blocks, S, parts, phase, st);
+    case 128: return fold_parts_r<128>(T, D, dY, lddy, P, p_blocks, S, parts, phase, st);
+    case 256: return fold_parts_r<256>(T, D, dY, lddy, P, p_blocks, S, parts, phase, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,

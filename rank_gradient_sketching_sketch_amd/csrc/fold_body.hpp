@@ -67,9 +67,12 @@ constexpr int kL1Bypass = 1;
 constexpr int kHwRegXccId = 20 | (0 << 6) | (3 << 11);
 
 // How the members of a tile add their partials: one member (nothing to
-// add); two, exchanging MFMA fragments within the kernel; or more, each
-// writing its partial tile for fold_reduce_kernel to add.
-enum FoldMode { kFoldSingle = 0, kFoldPair = 1, kFoldPartial = 2 };
+// add); two, exchanging MFMA fragments within the kernel; more, each
+// writing its partial tile for fold_reduce_kernel to add; or split: the
+// sketch is kept in parts across the microbatches of a step, member 0 adding
+// its partial to S and member q > 0 to part q - 1 (xbuf + (q - 1) d r), with
+// no exchange and no waiting inside the kernel.
+enum FoldMode { kFoldSingle = 0, kFoldPair = 1, kFoldPartial = 2, kFoldSplit = 3 };
 
 // The fold of one workgroup. smem (FoldShape::LDS_BYTES, 16-byte aligned) and
 // s_word are the caller's LDS; fixed_ticket >= 0 names the workgroup's tile
@@ -170,7 +173,7 @@ __device__ __forceinline__ void fold_body(
         own1 = mem == 0 ? min(16 * WM * kHalf, rows) : rows;
     } else {
         own0 = 0;
-        own1 = MODE == kFoldSingle ? rows : 0;
+        own1 = MODE == kFoldSingle || MODE == kFoldSplit ? rows : 0;
     }
 
 
@@ -183,8 +186,10 @@ __device__ __forceinline__ void fold_body(
     const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(P), 0, static_cast<int>(static_cast<int64_t>(p_blocks) * R * 64),
         0x00020000);
+    // the member's share of the sketch: S, or in split mode its part
+    float *dst = MODE == kFoldSplit && mem > 0 ? xbuf + static_cast<int64_t>(mem - 1) * D * R : S;
     const __amdgpu_buffer_rsrc_t s_rs =
-        __builtin_amdgcn_make_buffer_rsrc(S, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(dst, 0, static_cast<int>(static_cast<int64_t>(D) * R * 4), 0x00020000);
 
     // The (up to NCH) 16-byte dY chunks this thread moves per step. Chunk
     // counts are multiples of 64, so whether a wave has a chunk is uniform

@@ -45,6 +45,13 @@ struct FoldWait {
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, const FoldWait &wait, hipStream_t st);
+// Split-mode fold (the sketch of a step held as S plus n_split - 1 parts of
+// d x r fp32): phase bit 0 starts the step (S and the parts overwritten),
+// bit 1 ends it (the parts added into S afterwards, in part order).
+size_t fold_parts_bytes_bf16(int64_t T, int64_t D, int R);
+hipError_t launch_fold_parts_bf16(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
+                                  const uint16_t *P, int p_blocks, float *S, float *parts, int phase,
+                                  hipStream_t st);
 // The backward input gradient dX = dY W (bf16, 256 x 256 product tiles)
 // and, when sketch != 0, the fold S (+)= dY^T P in the same launch (P read
 // from the projection the sketch workspace holds).
@@ -88,6 +95,9 @@ hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t 
                                const uint16_t *X, int64_t ldx, void *ws, int concurrency, hipStream_t st);
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
                             float *S, int accumulate, void *ws, const FoldWait &wait, hipStream_t st);
+// The split-mode fold reading P from the sketch workspace.
+hipError_t launch_fold_parts_ws_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY,
+                                     int64_t lddy, float *S, float *parts, int phase, void *ws, hipStream_t st);
 hipError_t launch_project_f32(int R, int64_t T, int64_t K, uint64_t key, float c, const float *X,
                               int64_t ldx, void *ws, hipStream_t st);
 hipError_t launch_fold_f32(int R, int64_t T, int64_t D, const float *dY, int64_t lddy, float *S,

@@ -273,6 +273,13 @@ hipError_t launch_project_bf16(int R, int64_t T, int64_t D, int64_t K, uint64_t 
     }
 }
 
+hipError_t launch_fold_parts_ws_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY,
+                                     int64_t lddy, float *S, float *parts, int phase, void *ws, hipStream_t st) {
+    const Stage1Plan p = plan_stage1_bf16(T, K, R);
+    return launch_fold_parts_bf16(R, T, D, dY, lddy, static_cast<const uint16_t *>(ws), p.t_blocks, S, parts,
+                                  phase, st);
+}
+
 hipError_t launch_fold_bf16(int R, int64_t T, int64_t D, int64_t K, const uint16_t *dY, int64_t lddy,
                             float *S, int accumulate, void *ws, const FoldWait &wait, hipStream_t st) {
     switch (R) {

@@ -10,9 +10,14 @@ the library's kernels.
 
 A step, in the order the host drives it:
   1. sketch: for every microbatch (in order, as a backward pass produces
-     them) and every matrix, logra_sketch_project then logra_sketch_fold
-     (accumulate = 0 for the first microbatch). Matrix i runs on sketch lane
-     i mod n_sketch; each lane is a stream with its own workspace.
+     them) and every matrix, logra_sketch_project then the fold: for a
+     matrix that keeps its sketch in parts during the step (the `parts`
+     policy), logra_sketch_fold_parts with LOGRA_FOLD_FIRST on the first
+     microbatch and LOGRA_FOLD_LAST on the last, so that the workgroups
+     sharing a tile of S never wait for each other; otherwise
+     logra_sketch_fold (accumulate = 0 for the first microbatch). Matrix i
+     runs on sketch lane i mod n_sketch; each lane is a stream with its own
+     workspace.
   2. pass 1: logra_update_sqnorm for every matrix (v -> v'), in batches of
      up to 16 matrices per apply lane (logra_update_sqnorm_batch: two
      launches per batch), matrix i on apply lane i mod n_apply.
@@ -57,6 +62,7 @@ class Matrix:
     sq: Optional[torch.Tensor] = None
     rowsq: Optional[torch.Tensor] = None
     desc: Optional[B.MatrixDesc] = None
+    parts: Optional[torch.Tensor] = None
     lane: int = 0
     alane: int = 0
 
@@ -79,11 +85,15 @@ class Step:
     seed      the library seed of the sign matrices.
     rowsq     also keep every matrix's per-row sums of squares from pass 1
               (Matrix.rowsq), for callers that inspect them.
+    parts     which matrices hold their sketch in parts during the step:
+              "pair" (those whose fold tiles are shared by two workgroups:
+              one extra d x r array each), "all" (every matrix whose fold
+              splits its tiles: up to 31 arrays for small d), or "none".
     """
 
     def __init__(self, matrices: Sequence[Matrix], r: int, tokens: int, act_dtype: int,
                  device=None, sketch_lanes: int = 0, apply_lanes: int = 0,
-                 batch_pass1: bool = True, seed: int = 0, rowsq: bool = False):
+                 batch_pass1: bool = True, seed: int = 0, rowsq: bool = False, parts: str = "pair"):
         if not matrices:
             raise ValueError("a step needs at least one matrix")
         self.mats: List[Matrix] = list(matrices)
@@ -109,8 +119,15 @@ class Step:
                 "ws": torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev),
                 "sq_ws": torch.empty(max(16, sq_ws_bytes), dtype=torch.uint8, device=dev),
             })
+        if parts not in ("pair", "all", "none"):
+            raise ValueError("parts must be 'pair', 'all' or 'none'")
+        self.parts_bytes = 0
         for i, m in enumerate(self.mats):
             m.S = torch.empty(m.d, r, dtype=torch.float32, device=dev)
+            pb = B.logra_sketch_parts_bytes(B.MatrixDesc(m.d, m.k, r), tokens, act_dtype)
+            use = pb > 0 and (parts == "all" or (parts == "pair" and pb == 4 * m.d * r))
+            m.parts = torch.empty(pb // 4, dtype=torch.float32, device=dev) if use else None
+            self.parts_bytes += pb if use else 0
             m.v_new = torch.empty(m.d, dtype=torch.float32, device=dev)
             m.sq = torch.empty(1, dtype=torch.float32, device=dev)
             m.rowsq = torch.empty(m.d, dtype=torch.float32, device=dev) if rowsq else None
@@ -186,7 +203,13 @@ class Step:
                 B.logra_sketch_project(m.desc, X, ln["ws"], st, opts=self.sketch_opts)
                 if marks is not None:
                     marks.append(_event(st))
-                B.logra_sketch_fold(m.desc, dY, m.S, mb > 0, ln["ws"], st, opts=self.sketch_opts)
+                if m.parts is not None:
+                    phase = ((B.LOGRA_FOLD_FIRST if mb == 0 else 0)
+                             | (B.LOGRA_FOLD_LAST if mb == microbatches - 1 else 0))
+                    B.logra_sketch_fold_parts(m.desc, dY, m.S, m.parts, phase, ln["ws"], st,
+                                              opts=self.sketch_opts)
+                else:
+                    B.logra_sketch_fold(m.desc, dY, m.S, mb > 0, ln["ws"], st, opts=self.sketch_opts)
                 if marks is not None:
                     marks.append(_event(st))
                     events = ((marks[0], marks[1]), (marks[1], marks[2]))

@@ -40,14 +40,14 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
-    assert B.logra_abi_version() == 3
+    assert B.logra_abi_version() == 4
     assert B.logra_status_string(0) == "LOGRA_OK"
     assert B.logra_status_string(3) == "LOGRA_ERR_WORKSPACE"
     assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
 
 
 def test_no_process_wide_settings(lib):
-    # ABI 3 keeps no mutable global state: the former process-wide setters
+    # the library keeps no mutable global state: the former process-wide setters
     # are gone, their settings travel with each call in logra_launch_opts
     for name in ("logra_set_fold_wait_limit", "logra_set_sketch_concurrency", "logra_set_apply_concurrency"):
         assert not hasattr(lib, name), name
@@ -253,3 +253,42 @@ def test_sqnorm_batch_validation_and_workspace(lib):
     mixed = B._matrix_array([ms[0], B.MatrixDesc(512, 3584, 128), ms[2]])
     assert call(3, mixed) == 1                    # ranks differ
     assert B.logra_sqnorm_batch_workspace_bytes([], B.LOGRA_BF16) == 0
+
+
+def test_fold_parts_sizes_and_validation(lib):
+    # The parts are (n - 1) d x r fp32 where n workgroups share each tile of
+    # S: two at the 7B up shape (d = 18944, 4096 tokens), more for small d,
+    # one (no parts) for short token counts and on the fp32 path. Bad phases,
+    # missing or short parts and misaligned parts are refused before any
+    # launch.
+    from rank_gradient_sketching_sketch_amd import binding as B
+    r = ctypes.byref
+    up = B.MatrixDesc(18944, 3584, 256, 0, 0, 0)
+    assert B.logra_sketch_parts_bytes(up, 4096, B.LOGRA_BF16) == 18944 * 256 * 4
+    assert B.logra_sketch_parts_bytes(up, 4096, B.LOGRA_F32) == 0
+    assert B.logra_sketch_parts_bytes(up, 0, B.LOGRA_BF16) == 0
+    assert B.logra_sketch_parts_bytes(up, 128, B.LOGRA_BF16) == 0     # 4 steps: one member per tile
+    small = B.MatrixDesc(3584, 3584, 256, 0, 0, 0)
+    n_small = B.logra_sketch_parts_bytes(small, 4096, B.LOGRA_BF16) // (3584 * 256 * 4)
+    assert n_small >= 2
+    assert B.logra_sketch_parts_bytes(B.MatrixDesc(18944, 3584, 100, 0, 0, 0), 4096, B.LOGRA_BF16) == 0
+    m = B.MatrixDesc(18944, 3584, 256, 0, 0, 0)
+    T = 4096
+    ws = B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16)
+    need = 18944 * 256 * 4
+
+    def call(parts, pb, phase, opts=None):
+        return lib.logra_sketch_fold_parts(r(m), T, 1, FAKE, 18944, FAKE, parts, pb, phase, FAKE, ws, opts, None)
+
+    assert call(FAKE, need, 4) == 1
+    assert call(FAKE, need, -1) == 1
+    assert call(None, 0, 0) == 3
+    assert call(FAKE, need - 16, 1) == 3
+    assert call(ctypes.c_void_p(0x10008), need, 0) == 1
+    o = B.LaunchOpts()
+    o.sketch_concurrency = -2
+    assert call(FAKE, need, 0, r(o)) == 1
+    # the fold's own checks apply too (lddy < d)
+    assert lib.logra_sketch_fold_parts(r(m), T, 1, FAKE, 64, FAKE, FAKE, need, 0, FAKE, ws, None, None) == 1
+    # T == 0 in a middle microbatch launches nothing and needs no parts
+    assert lib.logra_sketch_fold_parts(r(m), 0, 1, None, 0, FAKE, None, 0, 0, None, 0, None, None) == 0

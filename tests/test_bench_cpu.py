@@ -63,6 +63,11 @@ def test_traffic_record_is_tied_to_the_fold_sources(monkeypatch):
     if rec is not None:
         assert rec["fold_bytes_per_dispatch"] > bench.fold_bytes_per_launch(4096, 18944, 256, True)
         assert rec["fold_sources_sha256"] == bench.fold_sources_sha256()
+    rec_fold = bench.fold_traffic_record("qwen7b_up", "logra_sketch_fold")
+    if rec_fold is not None:
+        assert rec_fold["fold_bytes_per_dispatch"] > bench.fold_bytes_per_launch(4096, 18944, 256, True)
+    assert bench.fold_traffic_record("qwen7b_up", "no_such_call") is None
     monkeypatch.setattr(bench, "fold_sources_sha256", lambda: "0" * 64)
     assert bench.fold_traffic_record("qwen7b_up") is None
+    assert bench.fold_traffic_record("qwen7b_up", "logra_sketch_fold") is None
     assert bench.fold_traffic_record("no_such_workload") is None

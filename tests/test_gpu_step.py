@@ -4,7 +4,9 @@ benchmark times: the matrices' sketch calls spread over four streams and
 their apply passes over three, the lane counts declared to the kernels in the
 launch options (64-token projection workgroups and the 128-workgroup pass 2
 where they apply), pass 1 batched per apply stream, the v / v' swap, and the
-fold's time-out counter.
+fold's time-out counter. The folds keep the sketch in parts during the
+step where the scheduler's policy says so (by default the matrices whose fold
+tiles two workgroups share; one test per policy covers every split).
 
 The oracle computes P = X A^T in full for every microbatch (as one fp64
 matmul) and everything after it on a seeded sample of rows plus the first and
@@ -34,7 +36,7 @@ def _rows(d, n, seed):
     return np.unique(np.concatenate([[0, d - 1], rng.choice(d, n, replace=False)]))
 
 
-def _run_and_check(wl, specs, steps, mbs, nrows=256, sketch_lanes=4, apply_lanes=3):
+def _run_and_check(wl, specs, steps, mbs, nrows=256, sketch_lanes=4, apply_lanes=3, parts="pair"):
     dev = device()
     code = B.LOGRA_BF16
     r, T = wl.r, wl.tokens
@@ -48,9 +50,11 @@ def _run_and_check(wl, specs, steps, mbs, nrows=256, sketch_lanes=4, apply_lanes
         refs.append({"rows": rows, "W": W_h.double().numpy()[rows], "W32": W_h.double().numpy()[rows],
                      "v": v_h.double().numpy()[rows], "allow": None})
     st = Step(mats, r, T, code, device=dev, sketch_lanes=sketch_lanes, apply_lanes=apply_lanes,
-              batch_pass1=True, rowsq=True)
-    say("step schedule: %d matrices, %d sketch / %d apply streams, %d batched pass-1 calls"
-        % (len(mats), st.n_sketch, st.n_apply, sum(1 for b in st.batches if b[2] is not None)))
+              batch_pass1=True, rowsq=True, parts=parts)
+    say("step schedule: %d matrices, %d sketch / %d apply streams, %d batched pass-1 calls, "
+        "%d matrices with parts (%s)"
+        % (len(mats), st.n_sketch, st.n_apply, sum(1 for b in st.batches if b[2] is not None),
+           sum(1 for m in mats if m.parts is not None), parts))
     hp = dict(beta2=f32(wl.beta2), eps=f32(wl.eps), lr=f32(wl.lr))
     for step in range(steps):
         # every input of the step on the GPU before the step starts
@@ -148,7 +152,17 @@ def test_step_27b_one_layer_two_carried_steps():
 
 def test_step_two_layers_share_lanes_and_batches():
     # Two 7B layers (14 matrices): several matrices per sketch stream and
-    # pass-1 batches of several matrices per apply stream, two microbatches.
+    # pass-1 batches of several matrices per apply stream, two microbatches,
+    # every split fold keeping its sketch in parts.
     wl = inputs.WORKLOADS["qwen7b_28layer"]
-    say("step qwen7b_28layer layers 0-1: 2 x 4096 tokens")
-    _run_and_check(wl, wl.matrices[:14], steps=1, mbs=2, nrows=128)
+    say("step qwen7b_28layer layers 0-1: 2 x 4096 tokens, parts for every split fold")
+    _run_and_check(wl, wl.matrices[:14], steps=1, mbs=2, nrows=128, parts="all")
+
+
+def test_step_qwen15b_set_all_parts_and_none():
+    # The 1.5B set with parts for every split fold, and with none (every fold
+    # adds into S, the members of a tile exchanging partials in the kernel)
+    wl = inputs.WORKLOADS["qwen1.5b_set"]
+    for policy in ("all", "none"):
+        say("step qwen1.5b_set, parts: %s" % policy)
+        _run_and_check(wl, wl.matrices, steps=1, mbs=wl.microbatches, parts=policy)
