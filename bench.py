@@ -25,6 +25,7 @@ its partner (its rows would be NaN).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -128,6 +129,9 @@ def parse():
                     help="streams the matrices' apply passes are spread over (0: 1 for one matrix, else 3)")
     ap.add_argument("--parts", default="pair", choices=("pair", "all", "none"),
                     help="which matrices keep their sketch in parts during the step (logra_sketch_fold_parts)")
+    ap.add_argument("--input-sets", type=int, default=0,
+                    help="one-matrix workloads: distinct per-step input sets rotated over the steps "
+                         "(0: as many as the input budget holds, up to one per step)")
     ap.add_argument("--no-batch", action="store_true",
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
     ap.add_argument("--no-backward", action="store_true",
@@ -214,6 +218,8 @@ def main():
                          for s in wl.matrices) * nmb
     fresh = len(wl.matrices) == 1
     step_sets = max(1, min(n_steps, INPUT_BUDGET_BYTES // max(1, per_step_bytes))) if fresh else 1
+    if fresh and args.input_sets > 0:
+        step_sets = min(step_sets, args.input_sets)
 
     def xkey(spec, step, mb):
         st = step % step_sets if fresh else 0
@@ -289,16 +295,27 @@ def main():
     for s in range(args.warmup):
         one_step(s, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        one_step(args.warmup + s, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # Pass 2 is timed from an event the host records just before launching
+    # it (after reading the sqnorms), so a host pause there would count as
+    # GPU time: no garbage collection inside the timed steps.
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            one_step(args.warmup + s, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
     timeouts = step_runner.fold_timeouts()
 
     tot = {"sketch": 0.0, "sqnorm": 0.0, "apply": 0.0}
+    per_step = {"sketch": [], "sqnorm": [], "apply": []}
     for kind, a, b in ev_log:
-        tot[kind] += a.elapsed_time(b)
+        t = a.elapsed_time(b)
+        tot[kind] += t
+        per_step[kind].append(t)
     K = args.steps
     sketch_ms = tot["sketch"] / K
     apply_ms = (tot["sqnorm"] + tot["apply"]) / K
@@ -337,10 +354,12 @@ def main():
                    "frac_mfma_peak": round(sketch_tflops / PEAK_BF16_TFLOPS, 4),
                    "ms_per_step": round(sketch_ms, 4),
                    "project_ms_per_launch": round(proj_ms, 5),
-                   "fold_ms_per_launch": round(fold_ms, 5)},
+                   "fold_ms_per_launch": round(fold_ms, 5),
+                   "ms_per_step_range": [round(min(per_step["sketch"]), 4), round(max(per_step["sketch"]), 4)]},
         "apply": {"GBps": round(apply_gbps, 1), "frac_hbm_peak": round(apply_gbps / PEAK_HBM_GBPS, 4),
                   "ms_per_step": round(apply_ms, 4),
                   "sqnorm_ms": round(tot["sqnorm"] / K, 5), "rowadam_ms": round(tot["apply"] / K, 5),
+                  "rowadam_ms_range": [round(min(per_step["apply"]), 5), round(max(per_step["apply"]), 5)],
                   "skipped_nonfinite": skipped[0]},
         "roofline": {"kernel": ("fold_bf16_kernel (logra_sketch_fold_parts, a middle microbatch)"
                                 if mats[big].parts is not None else "fold_bf16_kernel (logra_sketch_fold)"),
