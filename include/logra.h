@@ -342,7 +342,7 @@ logra_status logra_backward_dx_sketch(const logra_matrix *m, int64_t T, int act_
 /*
  * logra_sqnorm_workspace_bytes -- device workspace logra_update_sqnorm needs
  * (per-block partial sums of the sqnorm reduction; on the bf16 path also the
- * r x r Gram matrix of the signs and a counter that the call zeroes itself).
+ * r x r Gram matrix of the signs; the call zeroes what must start at zero).
  * 0 for invalid m. Calls that run at the same time need separate workspaces.
  */
 size_t logra_sqnorm_workspace_bytes(const logra_matrix *m, int compute_dtype);
@@ -442,8 +442,8 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
  * ws_bytes. The call allocates nothing and calls no allocating routine.
  * Limit: the workspace logra_update_sqnorm would need for m
  *   (logra_sqnorm_workspace_bytes(m, compute_dtype)) must not exceed
- *   LOGRA_NOALLOC_SCRATCH_BYTES (512 KiB: on the bf16 path d up to 6,287,360
- *   rows at r = 256 and 8,351,744 at r = 32; on the fp32 path d up to
+ *   LOGRA_NOALLOC_SCRATCH_BYTES (512 KiB: on the bf16 path d up to 6,291,456
+ *   rows at r = 256 and 8,355,840 at r = 32; on the fp32 path d up to
  *   1,048,576 rows at any r); larger m returns LOGRA_ERR_WORKSPACE and
  *   launches nothing.
  * Sharing: each device holds one copy of the scratch until the process ends,

@@ -35,7 +35,7 @@ float inv_sqrt_rank(int64_t r) { return 1.0f / sqrtf(static_cast<float>(r)); }
 size_t sqnorm_ws_bytes(const logra_matrix *m, int compute_dtype) {
     if (compute_dtype == LOGRA_BF16) {
         const SqnormPlan p = plan_sqnorm_bf16(m->d, m->k, static_cast<int>(m->r));
-        return p.partial_bytes + p.gram_bytes + p.counter_bytes;
+        return p.partial_bytes + p.gram_bytes;
     }
     return static_cast<size_t>(apply_blocks_f32(m->d)) * sizeof(float);
 }
@@ -496,7 +496,6 @@ logra_status logra_update_sqnorm_batch(int n, const logra_matrix *ms, int comput
         it.rowsq = rowsq ? rowsq[i] : nullptr;
         it.slots = reinterpret_cast<uint64_t *>(base);
         it.M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
-        it.counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
         it.key = stream_key(ms[i].seed, ms[i].step, ms[i].matrix_id);
         it.c = inv_sqrt_rank(ms[i].r);
         it.D = static_cast<int>(ms[i].d);

@@ -32,17 +32,14 @@ namespace logra {
 constexpr int kGramChunk = 64;   // 64-bit words per row per chunk
 
 __device__ __forceinline__ void gram_body(uint64_t key, int R, int K, uint16_t *__restrict__ M,
-                                          int *__restrict__ counter, uint64_t *__restrict__ slots, int n_slots,
-                                          int bx, int by) {
+                                          uint64_t *__restrict__ slots, int n_slots, int bx, int by) {
     __shared__ uint64_t wl[16][kGramChunk + 1];
     __shared__ uint64_t wm[16][kGramChunk + 1];
     const int tid = threadIdx.x;
-    // the rowsq kernel that follows counts its workgroups from zero and
-    // finds their partials by the mark each one sets in its slot
-    if (bx == 0 && by == 0) {
-        if (tid == 0) *counter = 0;
+    // the rowsq kernel that follows finds its workgroups' partials by the
+    // mark each one sets in its slot (and leaves the slots zero again)
+    if (bx == 0 && by == 0)
         for (int i = tid; i < n_slots; i += 256) slots[i] = 0;
-    }
     const int l0 = by * 16, m0 = bx * 16;
     const int tl = tid >> 4, tm = tid & 15;
     const int nb = (K + 63) / 64;
@@ -74,9 +71,8 @@ __device__ __forceinline__ void gram_body(uint64_t key, int R, int K, uint16_t *
 }
 
 __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, uint16_t *__restrict__ M,
-                                                   int *__restrict__ counter, uint64_t *__restrict__ slots,
-                                                   int n_slots) {
-    gram_body(key, R, K, M, counter, slots, n_slots, blockIdx.x, blockIdx.y);
+                                                   uint64_t *__restrict__ slots, int n_slots) {
+    gram_body(key, R, K, M, slots, n_slots, blockIdx.x, blockIdx.y);
 }
 
 // rowsq_i = c^2 (k ||S_i||^2 + sum_m S_im Y_im), Y^T = M_off S^T. A workgroup
@@ -93,13 +89,16 @@ __global__ __launch_bounds__(256) void gram_kernel(uint64_t key, int R, int K, u
 // and the four waves' partials are added per row in wave order. The
 // controller's sum ends in the same kernel: each workgroup publishes its
 // partial as one 64-bit agent-scope atomic store of (mark << 32 | bits) into
-// its own slot, then counts itself in. The last one to arrive reads every
+// its own slot and is done. Workgroup 0 (dispatched first) then reads every
 // slot with 64-bit atomic loads, polling each until its mark is set (a slot
 // is a single atomic location, so a marked value is that workgroup's partial
 // of this launch: no ordering between different locations is relied on),
 // adds the partials in index order (fixed, so the result does not depend on
-// the arrival order), and clears the slots and the counter for the next
-// call. The poll is bounded; if it gives up, sqnorm is NaN.
+// the order the workgroups finish in), and clears the slots for the next
+// call. No workgroup waits for an atomic's reply before it ends, and only
+// workgroup 0 waits at all, which needs nothing of the others but that
+// they run (it holds one compute unit while they do). The poll is bounded;
+// if it gives up, sqnorm is NaN.
 constexpr int kRowsqMaxBlocks = 8;   // 16-row blocks of S per workgroup (most)
 constexpr int kRowsqWGs = 256;       // target workgroups (one per compute unit)
 constexpr uint64_t kSlotMark = 1ull << 32;
@@ -110,8 +109,8 @@ __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, i
                                            const uint16_t *__restrict__ M, float c,
                                            const float *__restrict__ v, float beta2, float eps,
                                            float *__restrict__ v_new, float *__restrict__ rowsq,
-                                           uint64_t *__restrict__ slots, int bpw, int *__restrict__ counter,
-                                           float *__restrict__ sqnorm, int blk, int nblk) {
+                                           uint64_t *__restrict__ slots, int bpw, float *__restrict__ sqnorm,
+                                           int blk, int nblk) {
     constexpr int KS = R / 32;                    // 32-wide steps of the rank
     constexpr int NB = R / 16;                    // 16-row blocks of m
     constexpr int MPW = NB >= 4 ? NB / 4 : 1;     // blocks of m per wave
@@ -123,7 +122,6 @@ __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, i
     __shared__ float2 part[4][kMaxRows];          // per wave and row: (dot, squares)
     __shared__ float terms[4];
     __shared__ float red[256];
-    __shared__ int last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -218,12 +216,8 @@ __device__ __forceinline__ void rowsq_body(const float *__restrict__ S, int D, i
         const float pw = ((terms[0] + terms[1]) + terms[2]) + terms[3];
         __hip_atomic_store(slots + blk, kSlotMark | __float_as_uint(pw), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == nblk - 1;
-        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    if (!last) return;
+    if (blk != 0) return;
     // sqnorm = the partials added in a fixed order: strided per thread, then a tree
     float t = 0.f;
     bool ok = true;
@@ -253,21 +247,21 @@ __global__ __launch_bounds__(256) void rowsq_gram_kernel(const float *__restrict
                                                          float eps, float *__restrict__ v_new,
                                                          float *__restrict__ rowsq,
                                                          uint64_t *__restrict__ slots, int bpw,
-                                                         int *__restrict__ counter, float *__restrict__ sqnorm) {
-    rowsq_body<R>(S, D, K, M, c, v, beta2, eps, v_new, rowsq, slots, bpw, counter, sqnorm, blockIdx.x,
+                                                         float *__restrict__ sqnorm) {
+    rowsq_body<R>(S, D, K, M, c, v, beta2, eps, v_new, rowsq, slots, bpw, sqnorm, blockIdx.x,
                   gridDim.x);
 }
 
 // Pass 1 of several matrices of one rank in two launches: the Gram matrices
 // of all of them (grid z = matrix), then every matrix's row blocks in one
 // grid, each workgroup finding its matrix from the running block counts.
-// Each matrix keeps its own workspace slice, counter and sqnorm, and the
+// Each matrix keeps its own workspace slice and sqnorm, and the
 // per-matrix arithmetic is the single-matrix kernels' own, so the results
 // are bit-identical to calling them one matrix at a time.
 template <int R>
 __global__ __launch_bounds__(256) void gram_batch_kernel(SqnormBatch b) {
     const SqnormItem &it = b.item[blockIdx.z];
-    gram_body(it.key, R, it.K, it.M, it.counter, it.slots, it.n_wg, blockIdx.x, blockIdx.y);
+    gram_body(it.key, R, it.K, it.M, it.slots, it.n_wg, blockIdx.x, blockIdx.y);
 }
 
 template <int R>
@@ -276,7 +270,7 @@ __global__ __launch_bounds__(256) void rowsq_batch_kernel(SqnormBatch b) {
     while (j + 1 < b.n && static_cast<int>(blockIdx.x) >= b.item[j + 1].wg_begin) ++j;
     const SqnormItem &it = b.item[j];
     rowsq_body<R>(it.S, it.D, it.K, it.M, it.c, it.v, b.beta2, b.eps, it.v_new, it.rowsq, it.slots, it.bpw,
-                  it.counter, b.sqnorm + j, static_cast<int>(blockIdx.x) - it.wg_begin, it.n_wg);
+                  b.sqnorm + j, static_cast<int>(blockIdx.x) - it.wg_begin, it.n_wg);
 }
 
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
@@ -292,7 +286,6 @@ SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R) {
     const size_t align = 256;
     p.partial_bytes = (static_cast<size_t>(p.n_blocks) * 8 + align - 1) / align * align;
     p.gram_bytes = (static_cast<size_t>(R) * R * 2 + align - 1) / align * align;
-    p.counter_bytes = align;
     return p;
 }
 
@@ -302,15 +295,14 @@ static hipError_t sqnorm_r(const ApplyArgs &a, void *ws, int parts, hipStream_t 
     char *base = static_cast<char *>(ws);
     uint64_t *slots = reinterpret_cast<uint64_t *>(base);
     uint16_t *M = reinterpret_cast<uint16_t *>(base + p.partial_bytes);
-    int *counter = reinterpret_cast<int *>(base + p.partial_bytes + p.gram_bytes);
     const int K = static_cast<int>(a.K);
     if (parts & kSqnormGram)
-        hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, counter, slots,
+        hipLaunchKernelGGL(gram_kernel, dim3(R / 16, R / 16), dim3(256), 0, st, a.key, R, K, M, slots,
                            p.n_blocks);
     if (parts & kSqnormRows)
         hipLaunchKernelGGL(rowsq_gram_kernel<R>, dim3(p.n_blocks), dim3(256), 0, st, a.S,
                            static_cast<int>(a.D), K, M, a.c, a.v_in, a.beta2, a.eps, a.v_new_out, a.rowsq_out,
-                           slots, p.rows_per_block / 16, counter, a.sqnorm);
+                           slots, p.rows_per_block / 16, a.sqnorm);
     return hipGetLastError();
 }
 

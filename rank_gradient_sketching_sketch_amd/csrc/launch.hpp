@@ -74,14 +74,12 @@ int apply_blocks_f32(int64_t D);
 // Workspace of apply pass 1 with bf16 compute: one 64-bit slot per
 // workgroup for its partial of the controller's reduction (a mark in the
 // high word, the float's bits in the low word), then the r x r Gram matrix
-// of the signs (bf16), then the counter the last workgroup is found with
-// (slots and counter zeroed by the Gram kernel and left zero).
+// of the signs (bf16) (slots zeroed by the Gram kernel and left zero).
 struct SqnormPlan {
     int n_blocks = 0;         // workgroups of rowsq_gram_kernel
     int rows_per_block = 0;   // rows of S each of them owns
     size_t partial_bytes = 0;
     size_t gram_bytes = 0;
-    size_t counter_bytes = 0;   // arrival counter of the last-workgroup reduction
 };
 SqnormPlan plan_sqnorm_bf16(int64_t D, int64_t K, int R);
 
@@ -132,7 +130,6 @@ struct SqnormItem {
     float *rowsq = nullptr;        // may be null
     uint16_t *M = nullptr;         // Gram matrix in the item's workspace slice
     uint64_t *slots = nullptr;     // per-workgroup partial slots
-    int *counter = nullptr;
     uint64_t key = 0;
     float c = 0.f;
     int D = 0, K = 0;

@@ -71,9 +71,9 @@ def test_noalloc_pass1_validation_before_any_device_call(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
     r = ctypes.byref
     V2 = ctypes.c_void_p(0x20000)
-    big = B.MatrixDesc(6287360 + 16, 64, 256, 0, 0, 0)
+    big = B.MatrixDesc(6291456 + 16, 64, 256, 0, 0, 0)
     assert B.logra_sqnorm_workspace_bytes(big, B.LOGRA_BF16) > B.NOALLOC_SCRATCH_BYTES
-    ok = B.MatrixDesc(6287360, 64, 256, 0, 0, 0)
+    ok = B.MatrixDesc(6291456, 64, 256, 0, 0, 0)
     assert B.logra_sqnorm_workspace_bytes(ok, B.LOGRA_BF16) <= B.NOALLOC_SCRATCH_BYTES
 
     def call(mm, compute=1, beta2=0.9, eps=1e-8, v_new=V2, sqn=FAKE):

@@ -53,7 +53,7 @@ def test_noalloc_pass1_equals_workspace_pass1(compute):
 
 def test_noalloc_pass1_refuses_above_its_limit():
     dev = device()
-    d = 6287360 + 16
+    d = 6291456 + 16
     m = B.MatrixDesc(d, 64, 256)
     S = torch.empty(16, 256, device=dev)     # never read: the call is refused first
     v = torch.empty(16, device=dev)
