@@ -8,7 +8,9 @@ The arithmetic of the sketch and the RowAdam step lives in ``oracle.c``
 (plain fp64 C, built with gcc). This module only marshals numpy arrays into
 it; every array passed in is converted to a C-contiguous float64 (or
 int64/uint64) copy first. The host step controller's oracle is plain Python
-in ``oracle/controller.py``.
+in ``oracle/controller.py``, and the two-sided sketch variant's (fixed
+orthonormal Gaussian projections on both sides, moments of both sketches,
+pseudo-inverse coupling) is plain numpy in ``oracle/two_sided.py``.
 """
 from __future__ import annotations
 
