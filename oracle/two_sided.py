@@ -115,10 +115,20 @@ def normalized(m, v, eps: float):
     return m / (np.sqrt(v) + eps)
 
 
+# Relative cutoff of the pseudo-inverse per unit of rank: the sketches and
+# their moments are fp32 state, so singular values of the coupling matrix at
+# most r * eps(fp32) times the largest are below the precision of the data
+# (numpy's dtype-aware rule, max(shape) * eps, for fp32 arrays). Where the
+# true coupling matrix is singular (a gradient of rank below r) an untruncated
+# inverse would be set by that rounding noise.
+PINV_RCOND_PER_RANK = float(np.finfo(np.float32).eps)
+
+
 def coupling(U_R, P):
-    """C = (P^T U_R)^+ (r x r), numpy's SVD pseudo-inverse (singular values
-    up to max(r, r) * machine eps times the largest count as zero)."""
-    return np.linalg.pinv(P.T @ U_R)
+    """C = (P^T U_R)^+ (r x r) by numpy's SVD pseudo-inverse, singular values
+    at most r * eps(fp32) times the largest counted as zero."""
+    M = P.T @ U_R
+    return np.linalg.pinv(M, rcond=max(M.shape) * PINV_RCOND_PER_RANK)
 
 
 def reconstruct(U_L, U_R, P):

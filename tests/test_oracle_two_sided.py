@@ -163,3 +163,40 @@ def test_sqnorm_equals_the_gram_trace_form():
     C, U_L, U_R = out["C"], out["U_L"], out["U_R"]
     trace_form = float(np.sum((C.T @ (U_R.T @ U_R) @ C) * (U_L @ U_L.T)))
     assert abs(out["sqnorm"] - trace_form) < 1e-10 * abs(trace_form)
+
+
+def test_coupling_truncates_at_the_fp32_precision_of_the_data():
+    # U_R = P M0 with P orthonormal gives the coupling matrix M0 itself; with
+    # singular values 1, 1e-3, 1e-5, 1e-7 (r = 4: cutoff 4 * 2^-23 = 4.8e-7)
+    # the pseudo-inverse keeps the first three and drops the last, in closed
+    # form V diag(1, 1e3, 1e5, 0) U^T
+    rng = np.random.default_rng(12)
+    r = 4
+    Uo = ts.orthonormalize(rng.standard_normal((r, r)))
+    Vo = ts.orthonormalize(rng.standard_normal((r, r)))
+    s = np.array([1.0, 1e-3, 1e-5, 1e-7])
+    M0 = Uo @ np.diag(s) @ Vo.T
+    P = ts.projection(4, 4, 0, 40, r)
+    C = ts.coupling(P @ M0, P)
+    want = Vo @ np.diag([1.0, 1e3, 1e5, 0.0]) @ Uo.T
+    assert np.abs(C - want).max() < 1e-6 * np.abs(want).max()
+
+
+def test_low_rank_recovery_under_fp32_rounding_of_the_sketches():
+    # sketches of a rank-4 gradient stored in fp32: the truncated coupling
+    # drops the 28 directions where the coupling matrix holds rounding noise
+    # only (its norm is 1 / sigma_4, not 1 / (noise)), and returns the
+    # gradient to fp32 accuracy
+    rng = np.random.default_rng(13)
+    d, k, r = 200, 160, 32
+    G = rng.standard_normal((d, 4)) @ rng.standard_normal((4, k))
+    P = ts.projection(6, 1, 0, d, r)
+    Q = ts.projection(6, 1, 1, k, r)
+    S_L = (P.T @ G).astype(np.float32).astype(np.float64)
+    S_R = (G @ Q).astype(np.float32).astype(np.float64)
+    sv = np.linalg.svd(P.T @ S_R, compute_uv=False)
+    assert sv[4] < 1e-7 * sv[0] < sv[3]
+    C = ts.coupling(S_R, P)
+    assert abs(np.linalg.norm(C, 2) - 1 / sv[3]) < 1e-6 / sv[3]
+    G_hat = ts.reconstruct(S_L, S_R, P)
+    assert np.abs(G_hat - G).max() < 1e-6 * np.abs(G).max()
