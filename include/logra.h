@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LOGRA_ABI_VERSION 4
+#define LOGRA_ABI_VERSION 5
 
 typedef enum logra_status {
     LOGRA_OK = 0,
@@ -546,6 +546,105 @@ double logra_kl_budget_at(const logra_kl_budget *b, uint64_t step);
  */
 logra_status logra_kl_step_scale(const float *sqnorm, int64_t n, float lr, double fisher_scale,
                                  double delta, float *scales, double *kl_pred, double *kl_after);
+
+/*
+ * Two-sided sketch variant (the walk-through page "LoGRA Cuts LLM RL VRAM by
+ * 45.7%: Fit 27B on a Single Node", section "Low-Rank Gradient Sketches via
+ * Random Projections"). Instead of one d x r sketch with signs redrawn each
+ * step, the gradient G = dY^T X (d x k) of a matrix is kept as two sketches
+ * made with FIXED, orthonormalized Gaussian projections P (d x r) and
+ * Q (k x r):
+ *     S_L = P^T G (r x k),   S_R = G Q (d x r),
+ * each with a first and a second moment, and the update is rebuilt from them
+ * by pseudo-inverse coupling:
+ *     U = m / (sqrt(v) + eps) entrywise (for both sketches),
+ *     Ghat = U_R (P^T U_R)^+ U_L,   W -= lr * scale * Ghat.
+ * For raw sketches of a gradient of rank <= r, Ghat is the gradient itself.
+ * Readings where the page is silent (the library's): the moments are
+ * m' = beta1 m + (1 - beta1) S and v' = beta2 v + (1 - beta2) S^2 with no
+ * bias correction; the pseudo-inverse drops singular values at most
+ * 32 * 2^-23 times the largest (the sketches and moments are fp32 state;
+ * where the true coupling matrix is singular an untruncated inverse would be
+ * set by their rounding); the Gaussian entries and the projections are fixed
+ * as follows.
+ *   Gaussian entry (i, j) of side s (0: P, n = d; 1: Q, n = k): with
+ *   key = h(h(h(seed) ^ (0xFFFFFFFFFFFFFF00 + s)) ^ matrix_id) (the sign
+ *   hash's key with that step value) and out(c) = mix(key + c *
+ *   0x9E3779B97F4A7C15), c = 2 (32 i + j) + 1: u1 = ((out(c) >> 11) + 1)
+ *   2^-53, u2 = (out(c + 1) >> 11) 2^-53, z = sqrt(-2 ln u1) cos(2 pi u2).
+ *   The projection is the Q factor of that n x 32 matrix whose R factor has
+ *   a positive diagonal (computed in fp64 and stored in fp32).
+ * Only r = 32 (m->r == 32; the page names 16 or 32) and bf16 activations
+ * are built; d and k must be multiples of 8, at least 32 and below 2^20
+ * (the fold's exchange buffer is addressed through 32-bit views). S_L is stored
+ * TRANSPOSED, as a k x 32 fp32 row-major array (S_L^T); S_R is d x 32 fp32.
+ * The moments have the shapes of their sketches (m_L, v_L: k x 32; m_R,
+ * v_R: d x 32, fp32). m->step is not used: the projections are fixed.
+ *
+ * logra_ts_projection_bytes -- bytes of the buffer holding one side's
+ *   projection (n = d for side 0, n = k for side 1): the n x 32 fp32 matrix
+ *   first, then its bf16 copy in the layout the sketch kernels read, then
+ *   scratch of its construction. 0 for invalid arguments.
+ * logra_ts_make_projection -- builds side `side` (0 or 1) of matrix m into
+ *   proj (device, 16-byte aligned, >= logra_ts_projection_bytes bytes).
+ *   Done once per matrix; the buffer is read by the calls below and must
+ *   not change between them. Errors: INVALID_ARGUMENT (side, null or not
+ *   16-byte aligned proj), UNSUPPORTED (r != 32, d or k outside the range
+ *   above), WORKSPACE (proj_bytes too small).
+ */
+size_t logra_ts_projection_bytes(const logra_matrix *m, int side);
+logra_status logra_ts_make_projection(const logra_matrix *m, int side, void *proj, size_t proj_bytes,
+                                      void *stream);
+
+/*
+ * logra_ts_sketch_accumulate -- one microbatch of T tokens:
+ *     S_L^T (+)= X^T (dY P)   (k x 32),   S_R (+)= dY^T (X Q)   (d x 32),
+ *   "+=" when accumulate != 0, "=" otherwise. X: T x k bf16 (row stride
+ *   ldx), dY: T x d bf16 (row stride lddy), both 16-byte aligned with
+ *   strides that are multiples of 8. proj_P / proj_Q: the buffers of sides 0
+ *   and 1 made by logra_ts_make_projection for this matrix. X Q and dY P are
+ *   formed on the matrix cores with fp32 accumulation and rounded to bf16
+ *   (the sketch's fold then takes them as operands, as the one-sided path
+ *   does with its projection); S is accumulated in fp32.
+ *   ws: device, 16-byte aligned, >= logra_ts_sketch_workspace_bytes(m, T).
+ *   T = 0 leaves S untouched with accumulate != 0 and zeroes it otherwise.
+ *   opts: only fold_wait_limit and fold_timeouts are read (the folds that
+ *   split tall tiles over two token halves wait as in the one-sided fold).
+ *   Errors: INVALID_ARGUMENT (pointers, strides, alignment), UNSUPPORTED
+ *   (r != 32, shapes; views of X, dY past 2^31 bytes), WORKSPACE.
+ */
+size_t logra_ts_sketch_workspace_bytes(const logra_matrix *m, int64_t T);
+logra_status logra_ts_sketch_accumulate(const logra_matrix *m, int64_t T, const void *X, int64_t ldx,
+                                        const void *dY, int64_t lddy, const void *proj_P, const void *proj_Q,
+                                        float *S_L, float *S_R, int accumulate, void *ws, size_t ws_bytes,
+                                        const logra_launch_opts *opts, void *stream);
+
+/*
+ * logra_ts_update -- the step-time part before the controller: updates the
+ *   four moments in place from S_L^T and S_R, forms U_L, U_R, the coupling
+ *   C = (P^T U_R)^+ (fp64 one-sided Jacobi SVD of the 32 x 32 matrix, whose
+ *   Gram sums are taken in fp64) and B = U_R C into ws, and writes
+ *   sqnorm[0] = ||Ghat||_F^2 (device float; from the fp64 Gram matrices, for
+ *   the step controller). beta1, beta2 in [0, 1], eps >= 0.
+ *   ws: >= logra_ts_update_workspace_bytes(m) bytes, 16-byte aligned; it
+ *   holds what logra_ts_apply reads, so the apply call of this matrix must
+ *   come before ws is used again.
+ *   Errors: INVALID_ARGUMENT (pointers, aliasing moments, betas, eps),
+ *   UNSUPPORTED (r != 32, shapes), WORKSPACE.
+ * logra_ts_apply -- W -= lr * scale * Ghat with Ghat = B U_L from the
+ *   workspace of the preceding logra_ts_update of this matrix. The products
+ *   take each fp32 operand as a bf16 head plus a bf16 tail (three matrix-core
+ *   products), close to an fp32 product; W is bf16 (rounded to nearest once)
+ *   or fp32, row stride ldw (multiple of 8, 16-byte aligned).
+ *   Errors: INVALID_ARGUMENT (pointers, ldw, non-finite lr or scale),
+ *   UNSUPPORTED (w_dtype, r != 32, shapes), WORKSPACE.
+ */
+size_t logra_ts_update_workspace_bytes(const logra_matrix *m);
+logra_status logra_ts_update(const logra_matrix *m, const float *S_L, const float *S_R, const void *proj_P,
+                             float *m_L, float *v_L, float *m_R, float *v_R, float beta1, float beta2, float eps,
+                             float *sqnorm, void *ws, size_t ws_bytes, void *stream);
+logra_status logra_ts_apply(const logra_matrix *m, const void *ws, size_t ws_bytes, void *W, int w_dtype,
+                            int64_t ldw, float lr, float scale, void *stream);
 
 #ifdef __cplusplus
 }

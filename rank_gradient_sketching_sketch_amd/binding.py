@@ -134,6 +134,20 @@ def load_library():
     lib.logra_kl_budget_at.argtypes = [ctypes.POINTER(KLBudget), u64]
     lib.logra_kl_step_scale.restype = i32
     lib.logra_kl_step_scale.argtypes = [P, i64, f32, dbl, dbl, P, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
+    lib.logra_ts_projection_bytes.restype = sz
+    lib.logra_ts_projection_bytes.argtypes = [D, i32]
+    lib.logra_ts_make_projection.restype = i32
+    lib.logra_ts_make_projection.argtypes = [D, i32, P, sz, P]
+    lib.logra_ts_sketch_workspace_bytes.restype = sz
+    lib.logra_ts_sketch_workspace_bytes.argtypes = [D, i64]
+    lib.logra_ts_sketch_accumulate.restype = i32
+    lib.logra_ts_sketch_accumulate.argtypes = [D, i64, P, i64, P, i64, P, P, P, P, i32, P, sz, O, P]
+    lib.logra_ts_update_workspace_bytes.restype = sz
+    lib.logra_ts_update_workspace_bytes.argtypes = [D]
+    lib.logra_ts_update.restype = i32
+    lib.logra_ts_update.argtypes = [D, P, P, P, P, P, P, P, f32, f32, f32, P, P, sz, P]
+    lib.logra_ts_apply.restype = i32
+    lib.logra_ts_apply.argtypes = [D, P, sz, P, i32, i64, f32, f32, P]
     _lib = lib
     return lib
 
@@ -384,3 +398,63 @@ def logra_update_sqnorm_batch(ms, compute_dtype: int, S, v, beta2: float, eps: f
         ctypes.cast(_ptr_array(v), ctypes.POINTER(ctypes.c_void_p)), float(beta2), float(eps),
         ctypes.cast(_ptr_array(v_new), ctypes.POINTER(ctypes.c_void_p)), rq, _ptr(sqnorm), _ptr(ws),
         ws_bytes, _stream(stream)), "logra_update_sqnorm_batch")
+
+
+# ---- two-sided sketch variant (rank 32, bf16 activations) ----
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def logra_ts_projection_bytes(m: MatrixDesc, side: int) -> int:
+    return int(load_library().logra_ts_projection_bytes(ctypes.byref(m), int(side)))
+
+
+def logra_ts_make_projection(m: MatrixDesc, side: int, proj: torch.Tensor, stream=None) -> None:
+    """Builds side 0 (P, d x 32) or side 1 (Q, k x 32) of matrix m into proj."""
+    _check(load_library().logra_ts_make_projection(ctypes.byref(m), int(side), _ptr(proj), _nbytes(proj),
+                                                   _stream(stream)), "logra_ts_make_projection")
+
+
+def logra_ts_projection_fp32(m: MatrixDesc, side: int, proj: torch.Tensor) -> torch.Tensor:
+    """View of the n x 32 fp32 projection at the start of a projection buffer."""
+    n = m.d if side == 0 else m.k
+    return proj[:n * 32 * 4].view(torch.float32).view(n, 32)
+
+
+def logra_ts_sketch_workspace_bytes(m: MatrixDesc, T: int) -> int:
+    return int(load_library().logra_ts_sketch_workspace_bytes(ctypes.byref(m), int(T)))
+
+
+def logra_ts_sketch_accumulate(m: MatrixDesc, X: torch.Tensor, dY: torch.Tensor, proj_P: torch.Tensor,
+                               proj_Q: torch.Tensor, S_L: torch.Tensor, S_R: torch.Tensor, accumulate: bool,
+                               ws: Optional[torch.Tensor] = None, stream=None,
+                               opts: Optional[LaunchOpts] = None) -> None:
+    """S_L^T (+)= X^T (dY P) (k x 32), S_R (+)= dY^T (X Q) (d x 32)."""
+    T = X.shape[0]
+    if ws is None:
+        ws = torch.empty(max(16, logra_ts_sketch_workspace_bytes(m, T)), dtype=torch.uint8, device=X.device)
+    _check(load_library().logra_ts_sketch_accumulate(
+        ctypes.byref(m), T, _ptr(X), _ld(X), _ptr(dY), _ld(dY), _ptr(proj_P), _ptr(proj_Q), _ptr(S_L), _ptr(S_R),
+        1 if accumulate else 0, _ptr(ws), _nbytes(ws), _opts(opts), _stream(stream)),
+        "logra_ts_sketch_accumulate")
+
+
+def logra_ts_update_workspace_bytes(m: MatrixDesc) -> int:
+    return int(load_library().logra_ts_update_workspace_bytes(ctypes.byref(m)))
+
+
+def logra_ts_update(m: MatrixDesc, S_L, S_R, proj_P, m_L, v_L, m_R, v_R, beta1: float, beta2: float, eps: float,
+                    sqnorm: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """Moments in place, the coupling and B = U_R C into ws, sqnorm[0] = ||Ghat||^2."""
+    _check(load_library().logra_ts_update(
+        ctypes.byref(m), _ptr(S_L), _ptr(S_R), _ptr(proj_P), _ptr(m_L), _ptr(v_L), _ptr(m_R), _ptr(v_R),
+        float(beta1), float(beta2), float(eps), _ptr(sqnorm), _ptr(ws), _nbytes(ws), _stream(stream)),
+        "logra_ts_update")
+
+
+def logra_ts_apply(m: MatrixDesc, ws: torch.Tensor, W: torch.Tensor, lr: float, scale: float, stream=None) -> None:
+    """W -= lr * scale * Ghat from the workspace of the preceding logra_ts_update."""
+    _check(load_library().logra_ts_apply(
+        ctypes.byref(m), _ptr(ws), _nbytes(ws), _ptr(W), _dtype_code(W), _ld(W), float(lr), float(scale),
+        _stream(stream)), "logra_ts_apply")

@@ -534,4 +534,108 @@ logra_status logra_rowadam_apply(const logra_matrix *m, int compute_dtype, const
                                                 : launch_apply_f32(1, a, st));
 }
 
+// ------------------------------------------------------------- two-sided --
+
+// Step value of the projections' streams (side s uses this + s): one the
+// sign matrices of a run never take.
+constexpr uint64_t kTsProjectionStep = 0xFFFFFFFFFFFFFF00ull;
+
+static logra_status check_ts(const logra_matrix *m) {
+    if (!matrix_ok(m)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (m->r != 32 || m->d % 8 || m->k % 8 || m->d < 32 || m->k < 32) return LOGRA_ERR_UNSUPPORTED;
+    // the folds' exchange buffers are addressed through 32-bit views
+    if (!fits_view(m->d, m->r, 4 * 16) || !fits_view(m->k, m->r, 4 * 16)) return LOGRA_ERR_UNSUPPORTED;
+    return LOGRA_OK;
+}
+
+size_t logra_ts_projection_bytes(const logra_matrix *m, int side) {
+    if (check_ts(m) != LOGRA_OK || (side != 0 && side != 1)) return 0;
+    return ts_projection_layout(side ? m->k : m->d).total;
+}
+
+logra_status logra_ts_make_projection(const logra_matrix *m, int side, void *proj, size_t proj_bytes,
+                                      void *stream) {
+    if (side != 0 && side != 1) return LOGRA_ERR_INVALID_ARGUMENT;
+    logra_status e = check_ts(m);
+    if (e != LOGRA_OK) return e;
+    if (!proj || !aligned16(proj)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (proj_bytes < logra_ts_projection_bytes(m, side)) return LOGRA_ERR_WORKSPACE;
+    const uint64_t key = stream_key(m->seed, kTsProjectionStep + static_cast<uint64_t>(side), m->matrix_id);
+    return from_hip(launch_ts_projection(key, side ? m->k : m->d, proj, static_cast<hipStream_t>(stream)));
+}
+
+size_t logra_ts_sketch_workspace_bytes(const logra_matrix *m, int64_t T) {
+    if (check_ts(m) != LOGRA_OK || T <= 0 || T > (1ll << 30)) return 0;
+    return ts_sketch_layout(T, m->d, m->k).total;
+}
+
+logra_status logra_ts_sketch_accumulate(const logra_matrix *m, int64_t T, const void *X, int64_t ldx,
+                                        const void *dY, int64_t lddy, const void *proj_P, const void *proj_Q,
+                                        float *S_L, float *S_R, int accumulate, void *ws, size_t ws_bytes,
+                                        const logra_launch_opts *opts, void *stream) {
+    Opts o;
+    if (!read_opts(opts, &o)) return LOGRA_ERR_INVALID_ARGUMENT;
+    logra_status e = check_ts(m);
+    if (e != LOGRA_OK) return e;
+    if (T < 0) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (T > (1ll << 30)) return LOGRA_ERR_UNSUPPORTED;
+    if (!S_L || !S_R || S_L == S_R || !aligned16(S_L) || !aligned16(S_R)) return LOGRA_ERR_INVALID_ARGUMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        if (accumulate) return LOGRA_OK;
+        if (launch_fill_zero(S_R, m->d * m->r, st) != hipSuccess) return LOGRA_ERR_HIP;
+        return from_hip(launch_fill_zero(S_L, m->k * m->r, st));
+    }
+    if (!X || !dY || !proj_P || !proj_Q || !aligned16(proj_P) || !aligned16(proj_Q)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (ldx < m->k || ldx % 8 || !aligned16(X)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (lddy < m->d || lddy % 8 || !aligned16(dY)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!fits_view(T + 32, ldx, 2) || !fits_view(T + 32, lddy, 2)) return LOGRA_ERR_UNSUPPORTED;
+    const size_t need = logra_ts_sketch_workspace_bytes(m, T);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    return from_hip(launch_ts_sketch(T, m->d, m->k, static_cast<const uint16_t *>(X), ldx,
+                                     static_cast<const uint16_t *>(dY), lddy, proj_P, proj_Q, S_L, S_R,
+                                     accumulate ? 1 : 0, ws, o.wait, st));
+}
+
+size_t logra_ts_update_workspace_bytes(const logra_matrix *m) {
+    if (check_ts(m) != LOGRA_OK) return 0;
+    return ts_update_layout(m->d, m->k).total;
+}
+
+logra_status logra_ts_update(const logra_matrix *m, const float *S_L, const float *S_R, const void *proj_P,
+                             float *m_L, float *v_L, float *m_R, float *v_R, float beta1, float beta2, float eps,
+                             float *sqnorm, void *ws, size_t ws_bytes, void *stream) {
+    logra_status e = check_ts(m);
+    if (e != LOGRA_OK) return e;
+    const void *ptrs[] = {S_L, S_R, proj_P, m_L, v_L, m_R, v_R};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!sqnorm) return LOGRA_ERR_INVALID_ARGUMENT;
+    const void *outs[] = {m_L, v_L, m_R, v_R};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (outs[i] == outs[j]) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!(beta1 >= 0.f && beta1 <= 1.f) || !(beta2 >= 0.f && beta2 <= 1.f) || !(eps >= 0.f))
+        return LOGRA_ERR_INVALID_ARGUMENT;
+    const size_t need = logra_ts_update_workspace_bytes(m);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    return from_hip(launch_ts_update(m->d, m->k, S_L, S_R, proj_P, m_L, v_L, m_R, v_R, beta1, beta2, eps, sqnorm,
+                                     ws, static_cast<hipStream_t>(stream)));
+}
+
+logra_status logra_ts_apply(const logra_matrix *m, const void *ws, size_t ws_bytes, void *W, int w_dtype,
+                            int64_t ldw, float lr, float scale, void *stream) {
+    logra_status e = check_ts(m);
+    if (e != LOGRA_OK) return e;
+    if (!W) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (w_dtype != LOGRA_F32 && w_dtype != LOGRA_BF16) return LOGRA_ERR_UNSUPPORTED;
+    if (ldw < m->k || ldw % 8 || !aligned16(W)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(lr) || !isfinite(scale)) return LOGRA_ERR_INVALID_ARGUMENT;
+    if (!fits_view(m->d, ldw, w_dtype == LOGRA_BF16 ? 2 : 4)) return LOGRA_ERR_UNSUPPORTED;
+    const size_t need = logra_ts_update_workspace_bytes(m);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return LOGRA_ERR_WORKSPACE;
+    return from_hip(launch_ts_apply(m->d, m->k, ws, W, w_dtype == LOGRA_BF16 ? 1 : 0, ldw, lr * scale,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

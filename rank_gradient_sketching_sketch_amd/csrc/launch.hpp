@@ -156,4 +156,42 @@ hipError_t launch_rowadam_bf16(const ApplyArgs &a, int concurrency, hipStream_t 
 hipError_t launch_apply_f32(int mode, const ApplyArgs &a, hipStream_t st);
 hipError_t launch_sqnorm_final(const float *partials, int n, float *out, hipStream_t st);
 
+// The two-sided sketch variant (rank 32, bf16 activations).
+// Projection buffer of one side (n = d for P, n = k for Q): the n x 32 fp32
+// orthonormal matrix, its bf16 operand copy (32-row block s, column l, row e
+// at element (32 s + l) 32 + e), then scratch of its construction.
+struct TsProjLayout {
+    int n_blocks = 0;
+    size_t fp32_bytes = 0, frag_bytes = 0, z_bytes = 0, partial_bytes = 0, gram_bytes = 0, rinv_bytes = 0;
+    size_t total = 0;
+};
+TsProjLayout ts_projection_layout(int64_t n);
+hipError_t launch_ts_projection(uint64_t key, int64_t n, void *buf, hipStream_t st);
+// Sketch workspace: Xq and Yp (bf16, fold operand layout), the fp32 partials
+// of the projection kernel, then the scratch of each of the two folds.
+struct TsSketchLayout {
+    int p_blocks = 0;
+    int chunks[2] = {0, 0};           // column chunks of X (job 0) and dY (job 1)
+    size_t p_bytes = 0, part_bytes = 0;
+    FoldPlan fold[2];                 // S_R over d, S_L^T over k
+    size_t fold_off[2] = {0, 0};
+    size_t total = 0;
+};
+TsSketchLayout ts_sketch_layout(int64_t T, int64_t d, int64_t k);
+hipError_t launch_ts_sketch(int64_t T, int64_t d, int64_t k, const uint16_t *X, int64_t ldx, const uint16_t *dY,
+                            int64_t lddy, const void *projP, const void *projQ, float *S_L, float *S_R,
+                            int accumulate, void *ws, const FoldWait &wait, hipStream_t st);
+// Update workspace: U_R, U_L, B = U_R C, C, the three summed Gram matrices,
+// the per-block partials. It holds what the apply call reads.
+struct TsUpdateLayout {
+    int nr = 0, nl = 0;
+    size_t ur_off = 0, ul_off = 0, b_off = 0, c_off = 0, sums_off = 0, partial_off = 0, total = 0;
+};
+TsUpdateLayout ts_update_layout(int64_t d, int64_t k);
+hipError_t launch_ts_update(int64_t d, int64_t k, const float *S_L, const float *S_R, const void *projP, float *m_L,
+                            float *v_L, float *m_R, float *v_R, float beta1, float beta2, float eps, float *sqnorm,
+                            void *ws, hipStream_t st);
+hipError_t launch_ts_apply(int64_t d, int64_t k, const void *ws, void *W, int w_bf16, int64_t ldw, float step,
+                           hipStream_t st);
+
 }  // namespace logra

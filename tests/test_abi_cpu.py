@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     from rank_gradient_sketching_sketch_amd import binding as B
-    assert B.logra_abi_version() == 4
+    assert B.logra_abi_version() == 5
     assert B.logra_status_string(0) == "LOGRA_OK"
     assert B.logra_status_string(3) == "LOGRA_ERR_WORKSPACE"
     assert B.logra_status_string(99) == "LOGRA_UNKNOWN_STATUS"
