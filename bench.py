@@ -136,6 +136,8 @@ def parse():
                     help="pass 1 one matrix per call instead of batches of up to 16 per stream")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward dX product (alone and with the fold beside it)")
+    ap.add_argument("--no-two-sided", action="store_true",
+                    help="skip the two-sided sketch variant (rank 32) at the largest matrix's shape")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time torch.mm (the vendor GEMM) on the fold's contraction and on the "
                          "dense dY^T X it replaces, for context")
@@ -396,6 +398,11 @@ def main():
         spec = wl.matrices[big]
         result["backward_dx"] = backward_dx(wl, spec, mats[big].W, xbuf[xkey(spec, 0, 0)],
                                             [ybuf[ykey(spec, 0, mb)] for mb in range(min(nmb, 3))], fold_ms)
+    if code == B.LOGRA_BF16 and not args.no_two_sided:
+        spec = wl.matrices[big]
+        result["two_sided"] = two_sided(wl, spec, mats[big].W,
+                                        [xbuf[xkey(spec, 0, mb)] for mb in range(min(nmb, 3))],
+                                        [ybuf[ykey(spec, 0, mb)] for mb in range(min(nmb, 3))])
     if args.yardstick:
         result["yardstick"] = yardstick(wl, fold_ms if len(mats) == 1 else None)
     if not args.no_cpu_baseline:
@@ -461,6 +468,70 @@ def backward_dx(wl, spec, W, X, dYs, fold_ms, reps=15):
            "torch_mm_tflops": round(flop / med["torch_mm"] / 1e6, 1),
            "timing": "medians of %d alternating calls, one event pair each" % reps}
     del ws, S, dX
+    torch.cuda.empty_cache()
+    return out
+
+
+def two_sided(wl, spec, W, Xs, dYs, reps=20):
+    """The two-sided sketch variant (rank 32, fixed Gaussian projections) at
+    the largest matrix's shape and the workload's token count: `reps`
+    back-to-back sketch calls (alternating microbatches) between one event
+    pair, then `reps` update calls (moments, coupling, sqnorm), then `reps`
+    apply calls (on a copy of W), per-call averages; the projections'
+    one-time construction; and the step at the workload's microbatch count.
+    Byte rates count what the design moves: the sketch reads X and dY twice
+    (once to project them, once in the two folds), the apply reads and
+    writes W once."""
+    import torch
+    from rank_gradient_sketching_sketch_amd import binding as B
+    R = 32
+    T, d, k = wl.tokens, spec.d, spec.k
+    dev = W.device
+    m = B.MatrixDesc(d, k, R, seed=0, step=0, matrix_id=spec.matrix_id)
+    pP = torch.empty(B.logra_ts_projection_bytes(m, 0), dtype=torch.uint8, device=dev)
+    pQ = torch.empty(B.logra_ts_projection_bytes(m, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.logra_ts_sketch_workspace_bytes(m, T), dtype=torch.uint8, device=dev)
+    uws = torch.empty(B.logra_ts_update_workspace_bytes(m), dtype=torch.uint8, device=dev)
+    S_L = torch.zeros(k, R, device=dev)
+    S_R = torch.zeros(d, R, device=dev)
+    mom = [torch.zeros(n, R, device=dev) for n in (k, k, d, d)]
+    sq = torch.zeros(1, device=dev)
+    Wc = W.clone()
+
+    def bracket(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    proj_us = bracket(lambda i: (B.logra_ts_make_projection(m, 0, pP), B.logra_ts_make_projection(m, 1, pQ)), 1)
+    runs = {"sketch": lambda i: B.logra_ts_sketch_accumulate(m, Xs[i % len(Xs)], dYs[i % len(dYs)], pP, pQ,
+                                                             S_L, S_R, i > 0, ws),
+            "update": lambda i: B.logra_ts_update(m, S_L, S_R, pP, *mom, 0.9, 0.999, 1e-8, sq, uws),
+            "apply": lambda i: B.logra_ts_apply(m, uws, Wc, wl.lr, 1.0)}
+    for fn in runs.values():
+        bracket(fn, 3)
+    us = {name: bracket(fn, reps) for name, fn in runs.items()}
+    act = T * (d + k) * Xs[0].element_size()
+    wbytes = 2 * d * k * W.element_size()
+    nmb = wl.microbatches
+    out = {"shape_Tdk": [T, d, k], "r": R,
+           "projections_once_us": round(proj_us, 1),
+           "sketch_us_per_microbatch": round(us["sketch"], 2),
+           "sketch_GBps_two_reads": round(2 * act / us["sketch"] / 1e3, 1),
+           "update_us": round(us["update"], 2),
+           "apply_us": round(us["apply"], 2),
+           "apply_GBps": round(wbytes / us["apply"] / 1e3, 1),
+           "step_us": round(nmb * us["sketch"] + us["update"] + us["apply"], 1),
+           "microbatches": nmb,
+           "state_bytes": 3 * 4 * R * (d + k),
+           "timing": "one event pair around %d back-to-back calls of each kind" % reps}
+    del ws, uws, S_L, S_R, mom, Wc, pP, pQ
     torch.cuda.empty_cache()
     return out
 
