@@ -30,8 +30,8 @@
 //   * update (per step): moments of both sketches and the normalized sketches
 //     with per-block fp64 partials of U_R^T U_R, P^T U_R and U_L U_L^T; a tree
 //     sum; one workgroup for the pseudo-inverse C of the 32 x 32 coupling
-//     matrix M from the eigen-decomposition of M^T M by cyclic two-sided
-//     Jacobi (fp64; singular values at most 32 times the fp32 machine
+//     matrix M by cyclic one-sided Jacobi on its columns (fp64; singular
+//     values at most 32 times the fp32 machine
 //     epsilon 2^-23 times the largest count as zero: the sketches and
 //     moments are fp32, and where the true coupling matrix is singular an
 //     untruncated inverse would be set by their rounding) and the squared
@@ -488,127 +488,131 @@ __device__ __forceinline__ bool ts_rotation(double al, double be, double ga, dou
     return due;
 }
 
-// One workgroup, 256 threads. sums: [U_R^T U_R][P^T U_R][U_L U_L^T] (1024
-// doubles each). The pseudo-inverse of M = P^T U_R comes from the
-// eigen-decomposition H = M^T M = V Lambda V^T (cyclic two-sided Jacobi,
-// fp64): C = V Lambda^+ V^T M^T, where the eigenvalues with sqrt(lambda) at
-// most 32 2^-23 sqrt(lambda_max) count as zero (the singular values of M are
-// sqrt(lambda); fp64 rounding in H stays far below that cutoff). Each round
-// rotates 16 disjoint index pairs at once: thread (a, b) computes the
-// rotations of pairs a and b itself and forms block (a, b) of the rotated H
-// (into the other of two buffers) and rows 2a, 2a + 1 of V on pair b, so a
-// round needs one barrier; a sweep starts with a test of every pair and the
-// loop ends when none is due. Writes C (fp32) and sqnorm = ||U_R C U_L||_F^2.
-__global__ __launch_bounds__(256) void ts_couple_kernel(const double *__restrict__ sums, float *__restrict__ C_out,
-                                                        float *__restrict__ sqnorm) {
-    __shared__ double M[kTsR][kTsR + 1];
-    __shared__ double H[2][kTsR][kTsR + 1];
-    __shared__ double V[kTsR][kTsR + 1];
+// Sum over the 32 lanes of a half-wave by a butterfly of lane exchanges:
+// DPP quad swaps (lane ^ 1, lane ^ 2), the half-row and row mirrors (lane i
+// with 7 - i, then 15 - i: after the quad sums these pair up disjoint halves
+// just as xor 4 and xor 8 would) and a swizzle that swaps the two 16-lane
+// rows. Each stage adds two partial sums that are each other's mirror image
+// and fp64 addition commutes, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ double ts_dpp(double x) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF,
+                                               true);
+    return __longlong_as_double(static_cast<long long>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo)));
+}
+__device__ __forceinline__ double ts_swap16(double x) {
+    // bit-mask swizzle within 32 lanes: and 0x1F, or 0, xor 0x10
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const int lo = __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(u)), 0x401F);
+    const int hi = __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(u >> 32)), 0x401F);
+    return __longlong_as_double(static_cast<long long>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo)));
+}
+__device__ __forceinline__ double ts_half_wave_sum(double x) {
+    x += ts_dpp<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += ts_dpp<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += ts_dpp<0x141>(x);   // row_half_mirror
+    x += ts_dpp<0x140>(x);   // row_mirror
+    x += ts_swap16(x);
+    return x;
+}
+
+constexpr int kTsCoupleThreads = 512;   // 16 column pairs x 32 rows
+
+// One workgroup of 512 threads. sums: [U_R^T U_R][P^T U_R][U_L U_L^T] (1024
+// doubles each). The pseudo-inverse of M = P^T U_R by one-sided Jacobi on
+// its columns (fp64): A = M V converges to U Sigma, so the singular values
+// are A's column norms and C = V Sigma^+ U^T = sum_j v_j a_j^T / sigma_j^2
+// over the kept j (singular values at most 32 2^-23 times the largest count
+// as zero). A and V live in LDS column by column. A round rotates 16
+// disjoint column pairs at once: thread (pair, row) reads its row's entries
+// of the pair's two columns of A and of V, the pair's 32 threads (one
+// half-wave) add the three dot products by a butterfly, each computes the
+// same rotation and writes its four rotated entries back; one barrier per
+// round. The loop ends after a sweep in which no pair was due. Writes C
+// (fp32) and sqnorm = ||U_R C U_L||_F^2 (from the Gram matrices of U_R and
+// U_L, fp64).
+__global__ __launch_bounds__(kTsCoupleThreads) void ts_couple_kernel(const double *__restrict__ sums,
+                                                                     float *__restrict__ C_out,
+                                                                     float *__restrict__ sqnorm) {
+    __shared__ double A[kTsR][kTsR];          // A[col][row]
+    __shared__ double V[kTsR][kTsR];          // V[col][row]
     __shared__ double GR[kTsR][kTsR + 1];
     __shared__ double GL[kTsR][kTsR + 1];
-    __shared__ double X[kTsR][kTsR + 1];
     __shared__ double Cm[kTsR][kTsR + 1];
+    __shared__ double X[kTsR][kTsR + 1];
+    __shared__ double norm2[kTsR];
     __shared__ double inv[kTsR];
-    __shared__ double red[256];
+    __shared__ double red[kTsCoupleThreads];
     __shared__ int s_flag[3];
     const int tid = threadIdx.x;
-    for (int e = tid; e < kTsGram; e += 256) {
+    for (int e = tid; e < kTsGram; e += kTsCoupleThreads) {
         const int i = e >> 5, j = e & 31;
         GR[i][j] = sums[e];
-        M[i][j] = sums[kTsGram + e];
+        A[j][i] = sums[kTsGram + e];          // M[i][j]
         GL[i][j] = sums[2 * kTsGram + e];
-        V[i][j] = i == j ? 1.0 : 0.0;
+        V[j][i] = i == j ? 1.0 : 0.0;
     }
     if (tid < 3) s_flag[tid] = 0;
     __syncthreads();
-    for (int e = tid; e < kTsGram; e += 256) {
-        const int i = e >> 5, j = e & 31;
-        double h = 0.0;
-        for (int l = 0; l < kTsR; ++l) h += M[l][i] * M[l][j];
-        H[0][i][j] = h;
+    // ||M||_F^2, the scale of fp64 rounding in the dot products
+    if (tid < kTsR) {
+        double s2 = 0.0;
+        for (int i = 0; i < kTsR; ++i) s2 += A[tid][i] * A[tid][i];
+        norm2[tid] = s2;
     }
     __syncthreads();
     double tr = 0.0;
-    for (int j = 0; j < kTsR; ++j) tr += H[0][j][j];
+    for (int j = 0; j < kTsR; ++j) tr += norm2[j];
     const double floor_abs = 0x1p-52 * tr / kTsR;
-    const int a = tid >> 4, b = tid & 15;
-    int cur = 0;
+    const int k = tid >> 5, row = tid & 31;
     for (int sweep = 0; sweep < kTsMaxSweeps; ++sweep) {
-        // converged when no pair is due: then a sweep would change nothing
         if (tid == 0) s_flag[(sweep + 1) % 3] = 0;
-        for (int e = tid; e < kTsGram; e += 256) {
-            const int i = e >> 5, j = e & 31;
-            if (i < j && ts_rotation_due(H[cur][i][i], H[cur][j][j], H[cur][i][j], floor_abs)) s_flag[sweep % 3] = 1;
-        }
-        __syncthreads();
-        if (s_flag[sweep % 3] == 0) break;
         for (int round = 0; round < 31; ++round) {
-            const double(*Hc)[kTsR + 1] = H[cur];
-            double(*Hn)[kTsR + 1] = H[cur ^ 1];
-            int pa, qa, pb, qb;
-            ts_pair(round, a, pa, qa);
-            ts_pair(round, b, pb, qb);
-            // every read of the round first, then the arithmetic, then the writes
-            const double aal = Hc[pa][pa], abe = Hc[qa][qa], aga = Hc[pa][qa];
-            const double bal = Hc[pb][pb], bbe = Hc[qb][qb], bga = Hc[pb][qb];
-            const double h00 = Hc[pa][pb], h01 = Hc[pa][qb], h10 = Hc[qa][pb], h11 = Hc[qa][qb];
-            const int i0 = 2 * a, i1 = 2 * a + 1;
-            const double v0p = V[i0][pb], v0q = V[i0][qb], v1p = V[i1][pb], v1q = V[i1][qb];
-            double ca, sa, ta, cb, sb, tb;
-            ts_rotation(aal, abe, aga, floor_abs, ca, sa, ta);
-            const bool fb = ts_rotation(bal, bbe, bga, floor_abs, cb, sb, tb);
-            if (a == b) {
-                Hn[pb][pb] = fb ? bal - tb * bga : bal;
-                Hn[qb][qb] = fb ? bbe + tb * bga : bbe;
-                Hn[pb][qb] = fb ? 0.0 : bga;
-                Hn[qb][pb] = fb ? 0.0 : bga;
-            } else if (a < b) {
-                const double x00 = ca * h00 - sa * h10, x01 = ca * h01 - sa * h11;
-                const double x10 = sa * h00 + ca * h10, x11 = sa * h01 + ca * h11;
-                const double y00 = x00 * cb - x01 * sb, y01 = x00 * sb + x01 * cb;
-                const double y10 = x10 * cb - x11 * sb, y11 = x10 * sb + x11 * cb;
-                Hn[pa][pb] = y00;
-                Hn[pa][qb] = y01;
-                Hn[qa][pb] = y10;
-                Hn[qa][qb] = y11;
-                Hn[pb][pa] = y00;
-                Hn[qb][pa] = y01;
-                Hn[pb][qa] = y10;
-                Hn[qb][qa] = y11;
-            }
-            V[i0][pb] = cb * v0p - sb * v0q;
-            V[i0][qb] = sb * v0p + cb * v0q;
-            V[i1][pb] = cb * v1p - sb * v1q;
-            V[i1][qb] = sb * v1p + cb * v1q;
+            int p, q;
+            ts_pair(round, k, p, q);
+            const double ap = A[p][row], aq = A[q][row], vp = V[p][row], vq = V[q][row];
+            const double al = ts_half_wave_sum(ap * ap);
+            const double be = ts_half_wave_sum(aq * aq);
+            const double ga = ts_half_wave_sum(ap * aq);
+            double c, sn, t;
+            if (ts_rotation(al, be, ga, floor_abs, c, sn, t) && row == 0) s_flag[sweep % 3] = 1;
+            A[p][row] = c * ap - sn * aq;
+            A[q][row] = sn * ap + c * aq;
+            V[p][row] = c * vp - sn * vq;
+            V[q][row] = sn * vp + c * vq;
             __syncthreads();
-            cur ^= 1;
         }
+        // converged once a whole sweep found no pair due
+        if (s_flag[sweep % 3] == 0) break;
     }
-    // eigenvalues, the cutoff and X = M V
+    // singular values (column norms of A), the cutoff and 1 / sigma^2
     if (tid < kTsR) {
-        double smax = 0.0;
-        for (int j = 0; j < kTsR; ++j) smax = fmax(smax, sqrt(fmax(H[cur][j][j], 0.0)));
-        const double lam = H[cur][tid][tid];
-        inv[tid] = sqrt(fmax(lam, 0.0)) > 32.0 * 0x1p-23 * smax ? 1.0 / lam : 0.0;
-    }
-    for (int e = tid; e < kTsGram; e += 256) {
-        const int i = e >> 5, j = e & 31;
-        double x = 0.0;
-        for (int l = 0; l < kTsR; ++l) x += M[i][l] * V[l][j];
-        X[i][j] = x;
+        double s2 = 0.0;
+        for (int i = 0; i < kTsR; ++i) s2 += A[tid][i] * A[tid][i];
+        norm2[tid] = s2;
     }
     __syncthreads();
-    // C = V Lambda^+ (M V)^T
-    for (int e = tid; e < kTsGram; e += 256) {
-        const int i = e >> 5, j = e & 31;
+    if (tid < kTsR) {
+        double smax = 0.0;
+        for (int j = 0; j < kTsR; ++j) smax = fmax(smax, sqrt(norm2[j]));
+        inv[tid] = sqrt(norm2[tid]) > 32.0 * 0x1p-23 * smax ? 1.0 / norm2[tid] : 0.0;
+    }
+    __syncthreads();
+    // C[a][b] = sum_j V[a][j] A[b][j] / sigma_j^2
+    for (int e = tid; e < kTsGram; e += kTsCoupleThreads) {
+        const int a = e >> 5, b = e & 31;
         double c = 0.0;
-        for (int l = 0; l < kTsR; ++l) c += V[i][l] * (inv[l] * X[j][l]);
-        Cm[i][j] = c;
+        for (int j = 0; j < kTsR; ++j) c += V[j][a] * (inv[j] * A[j][b]);
+        Cm[a][b] = c;
         C_out[e] = static_cast<float>(c);
     }
     __syncthreads();
     // sqnorm = sum (C^T GR C) o GL, with X = GR C
-    for (int e = tid; e < kTsGram; e += 256) {
+    for (int e = tid; e < kTsGram; e += kTsCoupleThreads) {
         const int i = e >> 5, j = e & 31;
         double x = 0.0;
         for (int l = 0; l < kTsR; ++l) x += GR[i][l] * Cm[l][j];
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(256) void ts_couple_kernel(const double *__restrict
     }
     __syncthreads();
     double part = 0.0;
-    for (int e = tid; e < kTsGram; e += 256) {
+    for (int e = tid; e < kTsGram; e += kTsCoupleThreads) {
         const int i = e >> 5, j = e & 31;
         double x = 0.0;
         for (int l = 0; l < kTsR; ++l) x += Cm[l][i] * X[l][j];
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(256) void ts_couple_kernel(const double *__restrict
     }
     red[tid] = part;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = kTsCoupleThreads / 2; w > 0; w >>= 1) {
         if (tid < w) red[tid] += red[tid + w];
         __syncthreads();
     }
@@ -899,7 +903,7 @@ hipError_t launch_ts_update(int64_t d, int64_t k, const float *S_L, const float 
     sa.job[2] = TsSumJob{a.partials, 2 * kTsGram, L.nr, L.nl, sums + 2 * kTsGram};
     hipError_t e = launch_sum(sa, 3, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ts_couple_kernel, dim3(1), dim3(256), 0, st, sums, C, sqnorm);
+    hipLaunchKernelGGL(ts_couple_kernel, dim3(1), dim3(kTsCoupleThreads), 0, st, sums, C, sqnorm);
     hipLaunchKernelGGL(ts_b_kernel, dim3(static_cast<unsigned>((d + 63) / 64)), dim3(256), 0, st, a.U_R, C, d, Bm);
     return hipGetLastError();
 }
