@@ -13,7 +13,12 @@
 //     the token steps. Splitting the tokens of taller tiles cuts the P bytes
 //     per compute unit (for d = 18944: 128 tiles of 144-160 rows x 2 token
 //     halves rather than 256 tiles of 64-80 rows x all tokens), and dY is
-//     still read once. Kernel instances are built for tiles of at most 5 or
+//     still read once. Where the two halves would add their partials inside
+//     the kernel, the split is taken only where all of P is more than 1 MB
+//     per compute unit (T r > 2^19) or r = 256: below that the exchange and
+//     its waits cost more than the halved P bytes save (at d = 18944 and
+//     4096 tokens, r = 32: 48 -> 38 us per launch without the split; r = 256:
+//     the split stays). Kernel instances are built for tiles of at most 5 or
 //     at most 10 blocks; the waves compute every block of the instance but the
 //     last unconditionally (products past the tile are never stored), which
 //     keeps the unrolled steps free of branches.
@@ -93,16 +98,22 @@ __global__ __launch_bounds__(256) void fold_reduce_kernel(const float *__restric
     *dst = t;
 }
 
-FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R) {
+FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R, bool parts) {
     FoldPlan p;
     if (T <= 0) return p;
     p.nblk = static_cast<int>((D + 15) / 16);
     const int nsteps = static_cast<int>((T + 31) / 32);
     if (p.nblk >= 2 * kFoldWGs) {
-        // tiles over two token halves when there are enough steps to split,
-        // otherwise tiles over all tokens; at most 10 blocks a tile
+        // tiles over two token halves when there are enough steps to split
+        // and halving each member's projection bytes pays for the split
+        // (always with parts, which need no exchange; with the in-kernel
+        // exchange only where all of P is more than 1 MB per compute unit,
+        // T r > 2^19, or r = 256: below that the exchange and its waits cost
+        // more than the projection bytes they save), otherwise tiles over all
+        // tokens; at most 10 blocks a tile
         const int by_height = (p.nblk + 9) / 10;
-        if (nsteps >= 8) {
+        const bool split_pays = parts || R > 128 || T * static_cast<int64_t>(R) > (int64_t(1) << 19);
+        if (nsteps >= 8 && split_pays) {
             p.n_split = 2;
             p.n_tiles = by_height > kFoldWGs / 2 ? by_height : kFoldWGs / 2;
         } else {
@@ -177,7 +188,7 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
 template <int R>
 static hipError_t fold_parts_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy, const uint16_t *P,
                                int p_blocks, float *S, float *parts, int phase, hipStream_t st) {
-    const FoldPlan p = plan_fold_bf16(T, D, R);
+    const FoldPlan p = plan_fold_bf16(T, D, R, true);
     const int first = phase & 1, last = phase & 2;
     auto kernel = fold_bf16_kernel<R, 5, kFoldSingle>;
     if (p.n_split > 1)
@@ -196,7 +207,7 @@ static hipError_t fold_parts_r(int64_t T, int64_t D, const uint16_t *dY, int64_t
 }
 
 size_t fold_parts_bytes_bf16(int64_t T, int64_t D, int R) {
-    const FoldPlan p = plan_fold_bf16(T, D, R);
+    const FoldPlan p = plan_fold_bf16(T, D, R, true);
     return p.n_split > 1 ? static_cast<size_t>(p.n_split - 1) * D * R * 4 : 0;
 }
 

@@ -33,7 +33,10 @@ struct FoldPlan {
     size_t xbuf_bytes = 0;
     size_t sync_bytes = 0;
 };
-FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R);
+// parts: the plan of the split-mode fold (logra_sketch_fold_parts), whose
+// members never exchange; otherwise the plan of the fold whose members add
+// their partials inside the kernel.
+FoldPlan plan_fold_bf16(int64_t T, int64_t D, int R, bool parts = false);
 
 // How a fold member waits for its partner: at most spin_limit polls
 // (negative: give up at once), then its rows are written as NaN and

@@ -81,12 +81,14 @@ def test_sketch_bf16_matches_oracle(T, d, k, r, mbs):
 
 
 # Work splits of the fold: tiles over two token halves that exchange partial
-# tiles (d >= 8192), more workgroups than compute units (d > 20480), tall
-# tiles over all tokens when T has fewer than 8 steps of 32 (two epilogue
-# passes), and small d with 8 members per tile; ragged T and d throughout.
+# tiles (d >= 8192 at r = 256, or T r > 2^19), more workgroups than compute
+# units (d > 20480), tall tiles over all tokens (fewer than 8 steps of 32, or
+# r <= 128 with T r <= 2^19; two epilogue passes), and small d with 8 members
+# per tile; ragged T and d throughout.
 FOLD_SPLIT_CASES = [
     # T, d, k, r, microbatches
     (300, 8200, 136, 256, 2),
+    (4200, 8200, 64, 128, 1),     # T r > 2^19: two token halves at r = 128
     (4096, 512, 64, 256, 2),
     (200, 41000, 72, 32, 2),
     (257, 24008, 64, 64, 2),

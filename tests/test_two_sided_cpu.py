@@ -47,14 +47,17 @@ def test_projection_buffer_size(lib):
 def test_sketch_workspace_size(lib):
     # Xq and Yp (bf16, T rounded up to 32 tokens, x 32 columns), the fp32
     # partials of the projection kernel (one per 4096-column chunk of X and of
-    # dY), then the two folds' own scratch (a fold over d = 18944 rows splits
-    # 128 tiles over two token halves: exchange fragments and sync words)
+    # dY), then the two folds' own scratch: none for the fold over d = 18944
+    # rows (at r = 32 and 4096 tokens its tiles run over all tokens, one
+    # workgroup each), one d x 32 fp32 partial per member for the fold over
+    # k = 3584 (small d: several members per tile)
     m = B.MatrixDesc(18944, 3584, 32)
     T = 4096
     chunks = (3584 + 4095) // 4096 + (18944 + 4095) // 4096
     base = 2 * T * 32 * 2 + chunks * T * 32 * 4
     ws = B.logra_ts_sketch_workspace_bytes(m, T)
-    assert ws >= base + 128 * 2 * 160 * 32 * 4
+    members = (ws - base) // (3584 * 32 * 4)
+    assert ws == base + members * 3584 * 32 * 4 and 2 <= members <= 16
     assert B.logra_ts_sketch_workspace_bytes(m, 0) == 0
     assert B.logra_ts_sketch_workspace_bytes(B.MatrixDesc(18944, 3584, 256), T) == 0
     # ragged T rounds up to whole 32-token blocks
