@@ -342,3 +342,25 @@ def test_two_sided_step_is_bitwise_repeatable():
         assert torch.equal(x, y)
     assert all(torch.equal(x, y) for x, y in zip(a[4], b[4]))
     assert a[5] == b[5] and torch.equal(a[6], b[6])
+
+
+def test_sketch_with_strided_activations():
+    # X and dY as column slices of wider buffers (row strides k + 40 and
+    # d + 24): the same sketches as from contiguous copies, bit for bit, and
+    # within the bf16 tolerance of the oracle
+    dev = device()
+    T, d, k = 300, 1040, 520
+    m = B.MatrixDesc(d, k, R, seed=6, matrix_id=2)
+    pP, pQ = _proj(m, 0, dev), _proj(m, 1, dev)
+    Xs, dYs = _sketch_inputs(T, d, k, 2, 91, dev)
+    Xw = [torch.zeros(T, k + 40, dtype=torch.bfloat16, device=dev) for _ in Xs]
+    Yw = [torch.zeros(T, d + 24, dtype=torch.bfloat16, device=dev) for _ in dYs]
+    for a, b in zip(Xw, Xs):
+        a[:, :k] = b
+    for a, b in zip(Yw, dYs):
+        a[:, :d] = b
+    S_L, S_R = _sketch_run(m, [a[:, :k] for a in Xw], [a[:, :d] for a in Yw], pP, pQ, dev)
+    S_L2, S_R2 = _sketch_run(m, Xs, dYs, pP, pQ, dev)
+    assert torch.equal(S_L, S_L2) and torch.equal(S_R, S_R2)
+    L, Rs = _sketch_ref(m, Xs, dYs)
+    assert rownorm_err(to_f64(S_L), L.T) < BF16_TOL and rownorm_err(to_f64(S_R), Rs) < BF16_TOL
