@@ -13,10 +13,13 @@ rotate two sets per shape.
 
 Prints one JSON line. value = sketch-accumulate TFLOP/s (algorithmic
 2*T*r*(d+k) per microbatch call, over the HIP-event time of each step's
-sketch phase, one event pair per phase); the same line carries the
-RowAdam-apply GB/s (passes 1 and 2, the device-to-host read excluded), the
-roofline of the dominant kernel (the stage-2 fold: an event pair around one
-accumulating fold of every timed step, on the stream it runs on), its HBM
+sketch phase, one event pair per phase; every timing event here is created
+without the system-scope fence, which would add its cost to what it times);
+the same line carries the RowAdam-apply GB/s (passes 1 and 2, the
+device-to-host read excluded), the roofline of the dominant kernel (the
+stage-2 fold, one accumulating launch per timed step: a pair around its
+projection and it, less a pair around the projection before it alone, on
+the stream they run on), its HBM
 traffic from the committed profiler counters (when they were taken on the
 current fold sources), and the CPU oracle timed on a bounded sample of the
 same workload. Exits with status 3 if any fold workgroup gave up waiting for
@@ -188,7 +191,7 @@ def main():
 
     import torch
     from rank_gradient_sketching_sketch_amd import binding as B
-    from rank_gradient_sketching_sketch_amd import inputs
+    from rank_gradient_sketching_sketch_amd import hip_timing, inputs
     from rank_gradient_sketching_sketch_amd.step import Matrix, Step
 
     if not os.path.exists(B.LIB_PATH):
@@ -246,18 +249,20 @@ def main():
     apply_bytes = apply_bytes_per_step(wl)
 
     # The roofline's kernel: one accumulating fold per timed step (the
-    # largest matrix's, at the middle microbatch), bracketed by an event
-    # pair on the stream it runs on; the phases are bracketed on the main
-    # stream. Event records cost GPU time, so nothing else is bracketed.
+    # largest matrix's, at the middle microbatch), timed on the stream it
+    # runs on as the difference of two event pairs, one around that
+    # microbatch's projection and fold, one around the projection before it
+    # alone; the phases are bracketed on the main stream. Event records
+    # cost GPU time, so nothing else is bracketed.
     big = max(range(len(mats)), key=lambda i: mats[i].d * mats[i].k)
-    probe_mb = nmb // 2 if nmb > 1 else 0
+    if nmb < 2:
+        raise SystemExit("bench.py: the fold's timing needs at least two microbatches per step")
+    probe_mb = nmb // 2
     fold_events, proj_events = [], []
     ev_log = []   # (kind, start_event, end_event)
 
     def ev(stream):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        return e
+        return hip_timing.record(stream)
 
     def sketch_phase(step, timed):
         def get(i, mb):
@@ -323,8 +328,11 @@ def main():
     apply_ms = (tot["sqnorm"] + tot["apply"]) / K
     sketch_tflops = sketch_flop / (sketch_ms * 1e-3) / 1e12
     apply_gbps = apply_bytes / (apply_ms * 1e-3) / 1e9
-    fold_ms = sum(a.elapsed_time(b) for a, b in fold_events) / len(fold_events)
+    # the fold: the projection + fold pair less the projection-alone pair
+    # (each holds one event record's delay, which the difference cancels)
+    both_ms = sum(a.elapsed_time(b) for a, b in fold_events) / len(fold_events)
     proj_ms = sum(a.elapsed_time(b) for a, b in proj_events) / len(proj_events)
+    fold_ms = both_ms - proj_ms
     spec_big = wl.matrices[big]
     fold_bytes = fold_bytes_per_launch(T, spec_big.d, r, probe_mb > 0)
     fold_gbps = fold_bytes / (fold_ms * 1e-3) / 1e9
@@ -371,9 +379,11 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": fold_bytes,
                      "launch_us": round(fold_ms * 1e3, 2),
-                     "timing": "HIP event pair around one accumulating fold (matrix %s, microbatch %d) of "
-                               "every timed step, on its stream; %d launches" % (mats[big].name, probe_mb,
-                                                                                 len(fold_events)),
+                     "timing": "fence-free HIP events on the fold's stream in every timed step: a pair around "
+                               "the projection and accumulating fold of matrix %s, microbatch %d (%.2f us), less "
+                               "a pair around the projection of microbatch %d alone (%.2f us); %d steps"
+                               % (mats[big].name, probe_mb, both_ms * 1e3, probe_mb - 1, proj_ms * 1e3,
+                                  len(fold_events)),
                      "traffic_source": None if rec is None else rec.get("source")},
         "fold_timeouts": timeouts,
         "state_bytes": {"sketch_plus_v": sum(4 * s.d * r + 4 * s.d for s in wl.matrices),
@@ -425,6 +435,7 @@ def backward_dx(wl, spec, W, X, dYs, fold_ms, reps=15):
     import statistics
     import torch
     from rank_gradient_sketching_sketch_amd import binding as B
+    from rank_gradient_sketching_sketch_amd import hip_timing
     T, d, k, r = wl.tokens, spec.d, spec.k, wl.r
     dev = W.device
     m = B.MatrixDesc(d, k, r, seed=0, step=0, matrix_id=spec.matrix_id)
@@ -435,8 +446,7 @@ def backward_dx(wl, spec, W, X, dYs, fold_ms, reps=15):
     auto = B.LaunchOpts()
 
     def timed(fn, i):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a, b = hip_timing.FenceFreeEvent(), hip_timing.FenceFreeEvent()
         a.record()
         fn(i)
         b.record()
@@ -484,6 +494,7 @@ def two_sided(wl, spec, W, Xs, dYs, reps=20):
     writes W once."""
     import torch
     from rank_gradient_sketching_sketch_amd import binding as B
+    from rank_gradient_sketching_sketch_amd import hip_timing
     R = 32
     T, d, k = wl.tokens, spec.d, spec.k
     dev = W.device
@@ -499,8 +510,7 @@ def two_sided(wl, spec, W, Xs, dYs, reps=20):
     Wc = W.clone()
 
     def bracket(fn, n):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a, b = hip_timing.FenceFreeEvent(), hip_timing.FenceFreeEvent()
         torch.cuda.synchronize()
         a.record()
         for i in range(n):
@@ -556,6 +566,7 @@ def yardstick(wl, fold_ms):
     Operands are contiguous bf16 (dY^T materialised once), rotated over three
     sets so that no launch finds its inputs in the last-level cache."""
     import torch
+    from rank_gradient_sketching_sketch_amd import hip_timing
     spec = max(wl.matrices, key=lambda s: s.d * s.k)
     d, k, T, r = spec.d, spec.k, wl.tokens, wl.r
     g = torch.Generator(device="cuda:0")
@@ -570,8 +581,7 @@ def yardstick(wl, fold_ms):
         torch.cuda.synchronize()
         times = []
         for i in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a, b = hip_timing.FenceFreeEvent(), hip_timing.FenceFreeEvent()
             a.record()
             fn(i % 3)
             b.record()

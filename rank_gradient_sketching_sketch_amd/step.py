@@ -41,6 +41,7 @@ from typing import Callable, List, Optional, Sequence, Tuple
 import torch
 
 from . import binding as B
+from . import hip_timing
 
 MAX_SKETCH_LANES = 4   # HIP gives a process four hardware queues by default
 DEFAULT_APPLY_LANES = 3
@@ -68,9 +69,9 @@ class Matrix:
 
 
 def _event(stream):
-    e = torch.cuda.Event(enable_timing=True)
-    e.record(stream)
-    return e
+    # timing only: no system-scope fence, which would add its cost to the
+    # probed kernel's time and to the step
+    return hip_timing.record(stream)
 
 
 class Step:
@@ -186,9 +187,16 @@ class Step:
         """Fold `microbatches` microbatches into every matrix's S, microbatch
         by microbatch; inputs(i, mb) returns (X, dY) of matrix i.
 
-        probe = (i, mb): record timing events around matrix i's projection
-        and fold of microbatch mb, on the stream they run on; returns
-        ((project_start, project_end), (fold_start, fold_end)), else None."""
+        probe = (i, mb), mb >= 1: time matrix i's projection and fold
+        without an event between the two (an event record delays the next
+        kernel by a few microseconds): one event pair on its stream around
+        the projection of microbatch mb - 1 alone, one around the projection
+        and fold of microbatch mb; returns those two pairs,
+        ((project_start, project_end), (both_start, both_end)), else None.
+        The fold's time is the second pair's less the first's: each holds
+        one event record's delay."""
+        if probe is not None and probe[1] < 1:
+            raise ValueError("probe: the microbatch must have one before it")
         self.set_step(step)
         self._fork()
         events = None
@@ -197,12 +205,13 @@ class Step:
                 X, dY = inputs(i, mb)
                 ln = self.lanes[m.lane]
                 st = ln["stream"]
-                marks = [] if probe == (i, mb) else None
-                if marks is not None:
-                    marks.append(_event(st))
+                alone = probe == (i, mb + 1)     # the projection before the probed one
+                both = probe == (i, mb)
+                if alone or both:
+                    start = _event(st)
                 B.logra_sketch_project(m.desc, X, ln["ws"], st, opts=self.sketch_opts)
-                if marks is not None:
-                    marks.append(_event(st))
+                if alone:
+                    proj_pair = (start, _event(st))
                 if m.parts is not None:
                     phase = ((B.LOGRA_FOLD_FIRST if mb == 0 else 0)
                              | (B.LOGRA_FOLD_LAST if mb == microbatches - 1 else 0))
@@ -210,9 +219,8 @@ class Step:
                                               opts=self.sketch_opts)
                 else:
                     B.logra_sketch_fold(m.desc, dY, m.S, mb > 0, ln["ws"], st, opts=self.sketch_opts)
-                if marks is not None:
-                    marks.append(_event(st))
-                    events = ((marks[0], marks[1]), (marks[1], marks[2]))
+                if both:
+                    events = (proj_pair, (start, _event(st)))
         self._join()
         return events
 

@@ -166,3 +166,23 @@ def test_step_qwen15b_set_all_parts_and_none():
     for policy in ("all", "none"):
         say("step qwen1.5b_set, parts: %s" % policy)
         _run_and_check(wl, wl.matrices, steps=1, mbs=wl.microbatches, parts=policy)
+
+
+def test_fence_free_events_time_a_kernel():
+    # The step's probe events (created without the system-scope fence) and
+    # torch's ordinary events, nested around one spin kernel: the inner,
+    # fence-free pair sees the kernel run and holds no more than the outer.
+    from rank_gradient_sketching_sketch_amd import hip_timing
+    device()
+    torch.cuda.synchronize()
+    outer = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    inner = (hip_timing.FenceFreeEvent(), hip_timing.FenceFreeEvent())
+    outer[0].record()
+    inner[0].record()
+    torch.cuda._sleep(1_000_000)
+    inner[1].record()
+    outer[1].record()
+    torch.cuda.synchronize()
+    t_in, t_out = inner[0].elapsed_time(inner[1]), outer[0].elapsed_time(outer[1])
+    say("fence-free pair %.1f us, torch pair %.1f us" % (1e3 * t_in, 1e3 * t_out))
+    assert 0 < t_in <= t_out + 1e-3
