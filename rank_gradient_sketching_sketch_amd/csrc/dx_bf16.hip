@@ -38,15 +38,18 @@
 
 namespace logra {
 
-constexpr int kDxBM = 256, kDxBN = 256, kDxBK = 64;
-constexpr int kDxARow = kDxBK + 8;            // bf16 per dY row in LDS (144 bytes)
-constexpr int kDxBRow = kDxBN + 16;           // bf16 per W row in LDS (544 bytes)
-constexpr int kDxABytes = kDxBM * kDxARow * 2;
-constexpr int kDxBBytes = kDxBK * kDxBRow * 2;
-constexpr int kDxLds = 2 * (kDxABytes + kDxBBytes);
+constexpr int kDxBM = 256, kDxBN = 256, kDxBK = 32;
+constexpr int kDxStages = 4;                  // LDS ring: chunk c in stage c % 4
+constexpr int kDxAStage = kDxBM * kDxBK * 2;  // 256 token rows of 64 bytes
+constexpr int kDxBStage = kDxBK * kDxBN * 2;  // 32 rows of d, 512 bytes each
+constexpr int kDxStageBytes = kDxAStage + kDxBStage;
 constexpr int kDxCRow = kDxBN + 8;            // bf16 per row of the staged dX tile (528 bytes)
-static_assert(kDxBM * kDxCRow * 2 <= kDxLds, "the dX tile is staged in the operand buffers");
+constexpr int kDxCRowsPerStage = kDxBM / kDxStages;   // the dX tile is staged over the four stages
 constexpr int kDxFoldMaxB = 10;               // 16-row blocks per fold tile
+constexpr int kDxFoldStage = 32;              // rows per pass of the fold's epilogue (it has one stage of LDS)
+constexpr int kDxStageLds = kDxStageBytes > kDxCRowsPerStage * kDxCRow * 2 ? kDxStageBytes
+                                                                            : kDxCRowsPerStage * kDxCRow * 2;
+static_assert(FoldShape<256, kDxFoldMaxB, kDxFoldStage>::LDS_BYTES <= kDxStageLds, "the fold fits one stage");
 constexpr int kDxChipWGs = 256;               // one workgroup per compute unit
 constexpr int kDxFoldWGs = 32;                // fold workgroups beside a full grid of product tiles
 
@@ -69,7 +72,23 @@ struct DxArgs {
     int *timeouts;
 };
 
-__device__ __forceinline__ void dx_tile(char *smem, const DxArgs &a, int tm, int tn) {
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Swizzled stage layouts. The loads write LDS straight from memory, 1 KB per
+// wave instruction in lane order, so rows cannot be padded; instead the
+// 16-byte granules of a row are permuted, and each lane fetches the granule
+// that belongs at its position. A: token row t (4 granules of 8 d) keeps
+// granule q at q ^ ((t >> 2) & 3), so the 16 rows of a fragment read fall
+// on 16 different 16-byte bank groups. B: row j of d (32 granules of 8
+// columns) keeps granule q at q ^ dx_bsw(j), so the 8 rows that 32 lanes of
+// a transposed read touch (4 rows each of two 8-row groups) fall on 16
+// different bank groups for each pair of granules.
+__device__ __forceinline__ int dx_bsw(int j) { return ((j & 3) << 1) | (((j >> 3) & 1) << 3); }
+
+// The four stages are separate LDS arrays, so that the compiler can tell
+// the fragment reads of one stage from the loads still landing in the
+// others (with one array it waits for every load before each read).
+__device__ __forceinline__ void dx_tile(char *s0, char *s1, char *s2, char *s3, const DxArgs &a, int tm, int tn) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -82,42 +101,75 @@ __device__ __forceinline__ void dx_tile(char *smem, const DxArgs &a, int tm, int
         const_cast<uint16_t *>(a.W), 0, static_cast<int>(static_cast<int64_t>(a.D) * a.ldw * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t c_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.dX, 0, static_cast<int>(static_cast<int64_t>(a.T) * a.lddx * 2), 0x00020000);
-    uint16_t *lds_a[2] = {reinterpret_cast<uint16_t *>(smem),
-                          reinterpret_cast<uint16_t *>(smem + kDxABytes)};
-    uint16_t *lds_b[2] = {reinterpret_cast<uint16_t *>(smem + 2 * kDxABytes),
-                          reinterpret_cast<uint16_t *>(smem + 2 * kDxABytes + kDxBBytes)};
 
-    // This thread's 8 pieces of dY (rows tid / 8 + 32 j, columns 8 (tid % 8)
-    // .. +7 of the chunk) and 8 pieces of W (rows tid / 32 + 8 j, columns
-    // 8 (tid % 32) .. +7), j = 0..7: a base per thread plus uniform strides.
-    const int a_r0 = tid >> 3, a_c = 8 * (tid & 7);
-    const int b_r0 = tid >> 5, b_c = 8 * (tid & 31);
-    const uint32_t a_base = static_cast<uint32_t>((static_cast<int64_t>(t0 + a_r0) * a.lddy + a_c) * 2);
-    const uint32_t a_jstep = static_cast<uint32_t>(a.lddy * 2 * 32);
-    const uint32_t b_base = static_cast<uint32_t>((static_cast<int64_t>(b_r0) * a.ldw + n0 + b_c) * 2);
-    const uint32_t b_jstep = static_cast<uint32_t>(a.ldw * 2 * 8);
-    const uint32_t b_chunk_bytes = static_cast<uint32_t>(a.ldw * 2 * kDxBK);
-    const int a_rows_left = a.T - t0 - a_r0;          // piece j is a token when 32 j < a_rows_left
-    const bool b_col_ok = n0 + b_c < a.K;
-    const int a_l0 = a_r0 * kDxARow + a_c, b_l0 = b_r0 * kDxBRow + b_c;
-    auto load_chunk = [&](int c, u32x4_t (&ra)[8], u32x4_t (&rb)[8]) {
-        const int d0 = c * kDxBK;
-        const bool a_col_ok = d0 + a_c < a.D;
+    // The chunk's loads: wave w's instruction i fills 1 KB block 4 w + i of
+    // each operand's stage. A block: token rows 16 (4 w + i) .. +15, lane L
+    // at row 16 (4 w + i) + L / 4, position L % 4. B block: rows of d
+    // 2 (4 w + i) and +1, lane L at row 2 (4 w + i) + L / 32, position
+    // L % 32. A base offset per instruction plus a uniform step per chunk.
+    uint32_t a_off[4], b_off[4];
+    int a_q[4], b_row[4];
+    bool a_ok[4], b_ok[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t ao = (a_col_ok && 32 * j < a_rows_left) ? a_base + 2u * d0 + j * a_jstep : kOob;
-            ra[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ao, 0, 0));
-            const uint32_t bo = (b_col_ok && d0 + b_r0 + 8 * j < a.D)
-                                    ? b_base + static_cast<uint32_t>(c) * b_chunk_bytes + j * b_jstep
-                                    : kOob;
-            rb[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rs, bo, 0, 0));
+    for (int i = 0; i < 4; ++i) {
+        const int blk = 4 * wave + i;
+        const int ta = 16 * blk + (lane >> 2);
+        a_q[i] = (lane & 3) ^ ((ta >> 2) & 3);
+        a_ok[i] = t0 + ta < a.T;
+        a_off[i] = a_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(t0 + ta) * a.lddy + 8 * a_q[i]) * 2) : kOob;
+        const int jb = 2 * blk + (lane >> 5);
+        const int qb = (lane & 31) ^ dx_bsw(jb);
+        b_row[i] = jb;
+        b_ok[i] = n0 + 8 * qb < a.K;
+        b_off[i] = b_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(jb) * a.ldw + n0 + 8 * qb) * 2) : kOob;
+    }
+    const uint32_t b_chunk_bytes = static_cast<uint32_t>(a.ldw * 2 * kDxBK);
+    const int nck = (a.D + kDxBK - 1) / kDxBK;
+    // chunk c into stage S (c % 4); past the last chunk every offset is out
+    // of range and the stage is filled with zeros that are never read
+    // The chunk's step is the uniform (scalar) offset of the loads; a lane
+    // outside the operands takes the out-of-range offset, which no scalar
+    // offset brings back in range.
+    auto issue = [&](int c, auto stage_c) {
+        constexpr int S = decltype(stage_c)::value;
+        char *st = S == 0 ? s0 : S == 1 ? s1 : S == 2 ? s2 : s3;
+        const int d0 = c * kDxBK;
+        const int d_left = a.D - d0;   // <= 0 past the last chunk
+        // (no step past the last chunk: every lane is out of range there,
+        // and a step beyond the view must not wrap an offset back into it)
+        const int a_step = d_left > 0 ? 2 * d0 : 0;
+        const int b_step = d_left > 0 ? static_cast<int>(static_cast<uint32_t>(c) * b_chunk_bytes) : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t ao = 8 * a_q[i] < d_left ? a_off[i] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void_t *)(st + (4 * wave + i) * 1024), 16, ao, a_step,
+                                                     0, 0);
+            const uint32_t bo = b_row[i] < d_left ? b_off[i] : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void_t *)(st + kDxAStage + (4 * wave + i) * 1024), 16,
+                                                     bo, b_step, 0, 0);
         }
     };
-    auto store_chunk = [&](int buf, const u32x4_t (&ra)[8], const u32x4_t (&rb)[8]) {
+
+    // Operand fragments of one chunk (v_mfma_f32_16x16x32_bf16): A, row
+    // 128 wm + 16 mb + i16, d 8 g .. +7 (16 bytes); B, transposed reads of
+    // rows 8 g .. +7 of d, column 128 wn + 16 nb + i16.
+    auto read_frags = [&](auto stage_c, u32x4_t (&af)[8], u32x4_t (&bf)[8]) {
+        constexpr int S = decltype(stage_c)::value;
+        const char *A = S == 0 ? s0 : S == 1 ? s1 : S == 2 ? s2 : s3;
+        const char *Bm = A + kDxAStage;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<u32x4_t *>(lds_a[buf] + a_l0 + 32 * j * kDxARow) = ra[j];
-            *reinterpret_cast<u32x4_t *>(lds_b[buf] + b_l0 + 8 * j * kDxBRow) = rb[j];
+        for (int mb = 0; mb < 8; ++mb) {
+            const int t = 128 * wm + 16 * mb + i16;
+            af[mb] = *reinterpret_cast<const u32x4_t *>(A + t * 64 + ((g ^ ((t >> 2) & 3)) << 4));
+        }
+        const int j_lo = 8 * g + (i16 >> 2), j_hi = j_lo + 4;
+        const int sub = (i16 & 1) * 8;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int q = 16 * wn + 2 * nb + ((i16 & 3) >> 1);
+            const u32x2_t lo = lds_read_tr(reinterpret_cast<const uint16_t *>(Bm + j_lo * 512 + ((q ^ dx_bsw(j_lo)) << 4) + sub));
+            const u32x2_t hi = lds_read_tr(reinterpret_cast<const uint16_t *>(Bm + j_hi * 512 + ((q ^ dx_bsw(j_hi)) << 4) + sub));
+            bf[nb] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
         }
     };
 
@@ -127,90 +179,82 @@ __device__ __forceinline__ void dx_tile(char *smem, const DxArgs &a, int tm, int
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = zero_f32x4();
 
-    auto compute = [&](int buf) {
-        const uint16_t *A = lds_a[buf];
-        const uint16_t *Bm = lds_b[buf];
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // Pipeline: chunks 0..3 in flight, then per chunk c: wait until chunk
+    // c + 1 has landed (c + 2 and c + 3 may still be in flight) and the
+    // fragment reads of chunk c are done; a barrier, after which every wave
+    // has both (so stage c % 4 is free); the load of chunk c + 4 into it;
+    // then chunk c's 64 MFMAs with chunk c + 1's 24 fragment reads between
+    // them. Each wait is for loads issued three chunks earlier.
+    u32x4_t af[2][8], bfr[2][8];
+    issue(0, I0{});
+    issue(1, I1{});
+    issue(2, I2{});
+    issue(3, I3{});
+    __builtin_amdgcn_s_waitcnt(0x4078);   // vmcnt(24) expcnt(7) lgkmcnt(0): chunk 0 has landed
+    __builtin_amdgcn_s_barrier();
+    read_frags(I0{}, af[0], bfr[0]);
+    auto step = [&](int c, auto stage_c) {
+        constexpr int S = decltype(stage_c)::value;
+        constexpr int F = S & 1;
+        // vmcnt(16) expcnt(7) lgkmcnt(0): chunk c + 1 has landed, chunk c's
+        // fragments are in registers
+        __builtin_amdgcn_s_waitcnt(0x4070);
+        __builtin_amdgcn_s_barrier();
+        issue(c + 4, stage_c);
+        read_frags(std::integral_constant<int, (S + 1) & 3>{}, af[F ^ 1], bfr[F ^ 1]);
 #pragma unroll
-        for (int ks = 0; ks < kDxBK / 32; ++ks) {
-            u32x4_t af[8], bf[8];
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-                af[mb] = *reinterpret_cast<const u32x4_t *>(A + (128 * wm + 16 * mb + i16) * kDxARow + 32 * ks + 8 * g);
+            for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_bf16(af[F][mb], bfr[F][nb], acc[mb][nb]);
+        // one MFMA between each of the 8 loads and 24 fragment reads
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const uint16_t *p = Bm + (32 * ks + 8 * g + (i16 >> 2)) * kDxBRow + 128 * wn + 16 * nb + 4 * (i16 & 3);
-                const u32x2_t lo = lds_read_tr(p);
-                const u32x2_t hi = lds_read_tr(p + 4 * kDxBRow);
-                bf[nb] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-            }
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // load
+        }
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_bf16(af[mb], bf[nb], acc[mb][nb]);
+        for (int i = 0; i < 24; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         }
     };
-
-    // Register ring of two chunks: rg[c % 2] holds chunk c from its load
-    // (two chunks ahead) until it is stored into LDS buffer c % 2 (one ahead).
-    const int nck = (a.D + kDxBK - 1) / kDxBK;
-    u32x4_t rga[2][8], rgb[2][8];
-    load_chunk(0, rga[0], rgb[0]);
-    if (nck > 1) load_chunk(1, rga[1], rgb[1]);
-    store_chunk(0, rga[0], rgb[0]);
-    lds_barrier();
-    for (int c0 = 0; c0 < nck; c0 += 2) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = c0 + p;
-            if (c < nck) {
-                // Loads and stores are unconditional, so that the chunk is one
-                // block of code the scheduler can interleave (past the last
-                // chunk every offset is out of range and reads zero, and the
-                // buffer stored then is never read). With one wave per SIMD
-                // the matrix cores idle whenever the wave issues a run of
-                // other instructions; one MFMA between each of the chunk's 16
-                // global loads, 48 LDS reads and 16 LDS writes keeps them fed.
-                load_chunk(c + 2, rga[p], rgb[p]);
-                compute(p);
-                store_chunk(p ^ 1, rga[p ^ 1], rgb[p ^ 1]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
-                }
-#pragma unroll
-                for (int i = 0; i < 48; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-                }
-                lds_barrier();
-            }
-        }
+    for (int c0 = 0; c0 < nck; c0 += 4) {
+        step(c0, I0{});
+        if (c0 + 1 < nck) step(c0 + 1, I1{});
+        if (c0 + 2 < nck) step(c0 + 2, I2{});
+        if (c0 + 3 < nck) step(c0 + 3, I3{});
     }
 
     // dX tile: rounded to bf16, staged row-major in LDS, written as 16-byte
     // pieces of rows. Lane (i16, g) of block (mb, nb) holds rows
-    // 16 mb + 4 g + e, column 16 nb + i16 of its quarter.
-    uint16_t *ct = reinterpret_cast<uint16_t *>(smem);
+    // 16 mb + 4 g + e, column 16 nb + i16 of its quarter. The ring's last
+    // loads (zeros past the last chunk) land before the staging overwrites it.
+    // Tile rows 64 s .. 64 s + 63 go to stage s.
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    uint16_t *const ct[4] = {reinterpret_cast<uint16_t *>(s0), reinterpret_cast<uint16_t *>(s1),
+                             reinterpret_cast<uint16_t *>(s2), reinterpret_cast<uint16_t *>(s3)};
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int mb = 0; mb < 8; ++mb) {
+        uint16_t *cs = ct[2 * wm + mb / 4];
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                ct[(128 * wm + 16 * mb + 4 * g + e) * kDxCRow + 128 * wn + 16 * nb + i16] =
+                cs[(16 * (mb % 4) + 4 * g + e) * kDxCRow + 128 * wn + 16 * nb + i16] =
                     __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mb][nb][e]));
+    }
     lds_barrier();
 #pragma unroll 4
     for (int j = 0; j < (kDxBM * kDxBN / 8) / 256; ++j) {
         const int q = tid + 256 * j;
         const int row = q >> 5, col = 8 * (q & 31);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ct + row * kDxCRow + col);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ct[row / kDxCRowsPerStage] +
+                                                             (row % kDxCRowsPerStage) * kDxCRow + col);
         const uint32_t off = (t0 + row < a.T && n0 + col < a.K)
                                  ? static_cast<uint32_t>((static_cast<int64_t>(t0 + row) * a.lddx + n0 + col) * 2)
                                  : kOob;
@@ -220,8 +264,11 @@ __device__ __forceinline__ void dx_tile(char *smem, const DxArgs &a, int tm, int
 
 template <int R>
 __global__ __launch_bounds__(256) void dx_sketch_kernel(DxArgs a) {
-    constexpr int kFoldLds = FoldShape<R, kDxFoldMaxB>::LDS_BYTES;
-    __shared__ __attribute__((aligned(16))) char smem[kDxLds > kFoldLds ? kDxLds : kFoldLds];
+    static_assert(FoldShape<R, kDxFoldMaxB, kDxFoldStage>::LDS_BYTES <= kDxStageLds, "the fold fits one stage");
+    __shared__ __attribute__((aligned(16))) char s0[kDxStageLds];
+    __shared__ __attribute__((aligned(16))) char s1[kDxStageLds];
+    __shared__ __attribute__((aligned(16))) char s2[kDxStageLds];
+    __shared__ __attribute__((aligned(16))) char s3[kDxStageLds];
     __shared__ int s_word;
     const int id = static_cast<int>(blockIdx.x);
     if (id < a.n_fold) {
@@ -229,7 +276,8 @@ __global__ __launch_bounds__(256) void dx_sketch_kernel(DxArgs a) {
         // the sketch kernel's single-member mode
         const int nsteps = (a.T + 31) / 32;
         for (int t = id; t < a.fold_tiles; t += a.n_fold) {
-            fold_body<R, kDxFoldMaxB, kFoldSingle>(smem, s_word, t, a.dY, a.lddy, a.T, a.D, a.P, a.p_blocks, a.S,
+            fold_body<R, kDxFoldMaxB, kFoldSingle, kDxFoldStage>(s0, s_word, t, a.dY, a.lddy, a.T, a.D, a.P,
+                                                                 a.p_blocks, a.S,
                                                    nullptr, 0, nullptr, a.accumulate, a.fold_nblk, a.fold_tiles,
                                                    1, nsteps, a.spin_limit, a.timeouts);
             __syncthreads();   // the next tile's ring reuses the LDS
@@ -242,7 +290,7 @@ __global__ __launch_bounds__(256) void dx_sketch_kernel(DxArgs a) {
     const int gid = id - a.n_fold;
     const int G = a.n_tm * a.n_tn;
     const int tile = (G % kXcds == 0) ? (gid % kXcds) * (G / kXcds) + gid / kXcds : gid;
-    dx_tile(smem, a, tile / a.n_tn, tile % a.n_tn);
+    dx_tile(s0, s1, s2, s3, a, tile / a.n_tn, tile % a.n_tn);
 }
 
 DxPlan plan_dx_bf16(int64_t T, int64_t D, int64_t K, int sketch) {

@@ -21,7 +21,7 @@ constexpr int kFoldWGs = 256;         // one workgroup per compute unit
 // and the waves compute every block but the last unconditionally (products
 // of blocks past the tile are never stored), which keeps the unrolled steps
 // free of branches.
-template <int R, int MAXB>
+template <int R, int MAXB, int STAGE_ROWS = (R >= 256 ? 80 : 160)>
 struct FoldShape {
     static constexpr int NB = R / 16;            // 16-wide column blocks of r
     static constexpr int WN = NB < 4 ? NB : 4;   // waves across r
@@ -32,7 +32,7 @@ struct FoldShape {
     static constexpr int NCH = (32 * 2 * MAXB + 255) / 256;   // dY chunks per thread per step
     static constexpr int PF = MAXB > 5 ? 4 : 8;  // steps of dY and P held in registers ahead of use
     static constexpr int HALF = (MBW + 1) / 2;   // a wave's row blocks finalized by the first of two members
-    static constexpr int STAGE = R >= 256 ? 80 : 160;   // rows of the epilogue staging tile
+    static constexpr int STAGE = STAGE_ROWS;             // rows of the epilogue staging tile
     static constexpr int RING_BYTES = 3 * 32 * LDS_ROW * 2;             // the dY ring (kFoldSlots steps)
     static constexpr int TILE_BYTES = STAGE * (R + 4) * 4;              // the epilogue staging tile
     static constexpr int LDS_BYTES = RING_BYTES > TILE_BYTES ? RING_BYTES : TILE_BYTES;
@@ -79,13 +79,13 @@ enum FoldMode { kFoldSingle = 0, kFoldPair = 1, kFoldPartial = 2, kFoldSplit = 3
 // and member directly (single mode, used when the fold shares a launch with
 // other work), otherwise they come from the workgroup id (or, in pair mode,
 // from the ticket counter).
-template <int R, int MAXB, int MODE>
+template <int R, int MAXB, int MODE, int STAGE_ROWS = (R >= 256 ? 80 : 160)>
 __device__ __forceinline__ void fold_body(
     char *smem, int &s_word, int fixed_ticket,
     const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
     int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
     int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit, int *__restrict__ timeouts) {
-    using Sh = FoldShape<R, MAXB>;
+    using Sh = FoldShape<R, MAXB, STAGE_ROWS>;
     constexpr int NBW = Sh::NBW, MBW = Sh::MBW, WM = Sh::WM, PF = Sh::PF, NCH = Sh::NCH;
     constexpr int kLdsRow = Sh::LDS_ROW;
     constexpr int kSlot = 32 * kLdsRow;                 // one step: 32 token rows
