@@ -20,20 +20,16 @@
 //
 // Product tiles (v_mfma_f32_16x16x32_bf16). Four waves each own a 128 x 128
 // quarter of the tile (8 x 8 accumulator blocks, 256 registers). The
-// contraction over d runs in chunks of 64: every thread moves 8 16-byte
-// pieces of dY (256 tokens x 64) and 8 of W (64 x 256 columns) per chunk from
-// HBM into registers two chunks ahead of use, then into one of two LDS
-// buffers, so each wait is for a load issued two chunks earlier. dY rows
-// (144 bytes with padding, so the 16 rows of a fragment read fall on
-// different banks) give the A operand as 16-byte reads; W rows are read
+// contraction over d runs in chunks of 32 through a ring of four LDS stages:
+// buffer loads that write LDS directly fill chunk c + 4 while chunk c is
+// multiplied, so each wait is for loads issued three chunks earlier, and the
+// next chunk's operand fragments are read between the current chunk's
+// MFMAs. dY rows give the A operand as 16-byte reads; W rows are read
 // transposed with ds_read_b64_tr_b16, the B operand (8 consecutive d of one
 // column per lane). Loads go through buffer views: tokens past T, rows past
 // d and columns past k read as zero and are not written. The finished tile
 // is rounded to bf16 (nearest even), staged in LDS and written as whole
-// 16-byte pieces of dX rows. With one wave per SIMD the chunk's global
-// loads, LDS reads and LDS writes are interleaved one by one with its MFMAs
-// (scheduling barriers), which took the product at the 7B up shape from
-// 690 to 564 us.
+// 16-byte pieces of dX rows.
 #include "fold_body.hpp"
 
 namespace logra {
