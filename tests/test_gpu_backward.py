@@ -49,6 +49,9 @@ SMALL = [
     (1000, 8200, 136, 128, 2),
     (256, 256, 256, 256, 1),
     (520, 3000, 776, 256, 1),
+    # d % 32 == 16 (a partial last chunk of the product's 32-wide ones) and
+    # 11 chunks (three past a multiple of four), fewer tokens than one tile
+    (200, 336, 392, 64, 1),
 ]
 
 
@@ -118,6 +121,33 @@ def test_backward_dx_sketch_at_7b_shapes(d, k, ntok):
     e_s = rownorm_err(to_f64(S)[srows], S_ref)
     say("  dX %.3e  S %.3e" % (e_dx, e_s))
     assert e_dx < BF16_TOL and e_s < BF16_TOL
+
+
+def test_strided_operands_give_the_contiguous_result():
+    # dY, W and dX as column slices of wider tensors (leading dimensions
+    # past d and k, multiples of 8): the same bits as contiguous operands,
+    # with the fold in the launch and after it
+    dev = device()
+    T, d, k, r = 300, 1032, 264, 64
+    m = B.MatrixDesc(d, k, r, seed=6, step=1, matrix_id=2)
+    X, dY, W = _case(T, d, k, r, 77, dev)
+    dY_w = torch.zeros(T, d + 24, dtype=torch.bfloat16, device=dev)
+    W_w = torch.zeros(d, k + 40, dtype=torch.bfloat16, device=dev)
+    dY_w[:, :d] = dY
+    W_w[:, :k] = W
+    dYs, Ws = dY_w[:, :d], W_w[:, :k]
+    for placement in (1, 2):
+        say("backward dx strided", T, d, k, r, placement)
+        S, dX, dX0 = _run(m, X, dY, W, dev, 1, placement)
+        ws = torch.empty(B.logra_sketch_workspace_bytes(m, T, B.LOGRA_BF16), dtype=torch.uint8, device=dev)
+        S_s = torch.full((d, r), float("nan"), device=dev)
+        dX_w = torch.full((T, k + 16), float("nan"), dtype=torch.bfloat16, device=dev)
+        B.logra_sketch_project(m, X, ws)
+        B.logra_backward_dx_sketch(m, dYs, Ws, dX_w[:, :k], S_s, False, ws, opts=B.LaunchOpts(backward_fold=placement))
+        torch.cuda.synchronize()
+        assert torch.equal(dX_w[:, :k], dX)
+        assert torch.isnan(dX_w[:, k:].float()).all()   # the columns past k are not written
+        assert torch.equal(S_s, S)
 
 
 def test_backward_errors_leave_outputs_untouched():
