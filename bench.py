@@ -49,7 +49,8 @@ METRIC = "sketch-accum TFLOP/s + RowAdam-apply GB/s at 7B shapes, r=256; % of ro
 # while these are unchanged since the counters were taken.
 FOLD_SOURCES = ("rank_gradient_sketching_sketch_amd/csrc/fold_bf16.hip",
                 "rank_gradient_sketching_sketch_amd/csrc/fold_body.hpp",
-                "rank_gradient_sketching_sketch_amd/csrc/common.hpp")
+                "rank_gradient_sketching_sketch_amd/csrc/common.hpp",
+                "rank_gradient_sketching_sketch_amd/build_lib.py")
 # Predicted-KL controller run on every step's sqnorms and reported: an
 # isotropic Fisher of scale 1 and a budget annealed from 1e-3 to 1e-4 nats
 # over 1000 steps (the pages give no values). The update itself uses the

@@ -69,20 +69,16 @@
 //     partial to S, member q > 0 to part q - 1, each over the whole tile, so
 //     members neither exchange nor wait; the step's last fold then adds the
 //     parts into S in part order (fold_reduce_kernel).
+//
+// This file is compiled with the accumulators in vector registers rather
+// than the accumulation registers (the build's per-file flag): the unrolled
+// loop then keeps each accumulator where it is instead of rotating values
+// between the two register files, which made the split- and single-mode
+// folds about 3 % faster. The pair-mode instances run slower that way and
+// are built in fold_pair_bf16.hip without it.
 #include "fold_body.hpp"
 
 namespace logra {
-
-template <int R, int MAXB, int MODE>
-__global__ __launch_bounds__(256) void fold_bf16_kernel(
-    const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
-    int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
-    int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit, int *__restrict__ timeouts) {
-    __shared__ __attribute__((aligned(16))) char smem[FoldShape<R, MAXB>::LDS_BYTES];
-    __shared__ int s_word;
-    fold_body<R, MAXB, MODE>(smem, s_word, -1, dY, lddy, T, D, P, p_blocks, S, xbuf, x_bytes, sync, accumulate,
-                             nblk, n_tiles, n_split, steps_per, spin_limit, timeouts);
-}
 
 // S = [S +] (part_0 + part_1 + ...): the members' partial tiles added in
 // member order (small d, more than two members per tile).
@@ -167,11 +163,14 @@ static hipError_t fold_r(int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
     const FoldPlan p = plan_fold_bf16(T, D, R);
     float *xbuf = static_cast<float *>(scratch);
     int *sync = reinterpret_cast<int *>(static_cast<char *>(scratch) + p.xbuf_bytes);
+    if (p.n_split == 2)
+        return launch_fold_pair_bf16(R, p.max_blocks, p.n_tiles * p.n_split, st, dY, lddy, static_cast<int>(T),
+                                     static_cast<int>(D), P, p_blocks, S, xbuf, static_cast<int>(p.xbuf_bytes), sync,
+                                     accumulate, p.nblk, p.n_tiles, p.n_split, p.steps_per, wait.spin_limit,
+                                     wait.timeouts);
     auto kernel = fold_bf16_kernel<R, 5, kFoldSingle>;
     if (p.n_split > 2)
         kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldPartial> : fold_bf16_kernel<R, 10, kFoldPartial>;
-    else if (p.n_split == 2)
-        kernel = p.max_blocks == 5 ? fold_bf16_kernel<R, 5, kFoldPair> : fold_bf16_kernel<R, 10, kFoldPair>;
     else if (p.max_blocks == 10)
         kernel = fold_bf16_kernel<R, 10, kFoldSingle>;
     hipLaunchKernelGGL(kernel, dim3(p.n_tiles * p.n_split), dim3(256), 0, st, dY, lddy, static_cast<int>(T),

@@ -536,4 +536,17 @@ __device__ __forceinline__ void fold_body(
     }
 }
 
+// The fold kernel: one workgroup of four waves per tile member (FoldShape,
+// fold_body); the design is described at the top of fold_bf16.hip.
+template <int R, int MAXB, int MODE>
+__global__ __launch_bounds__(256) void fold_bf16_kernel(
+    const uint16_t *__restrict__ dY, int64_t lddy, int T, int D, const uint16_t *__restrict__ P,
+    int p_blocks, float *__restrict__ S, float *__restrict__ xbuf, int x_bytes, int *__restrict__ sync,
+    int accumulate, int nblk, int n_tiles, int n_split, int steps_per, int spin_limit, int *__restrict__ timeouts) {
+    __shared__ __attribute__((aligned(16))) char smem[FoldShape<R, MAXB>::LDS_BYTES];
+    __shared__ int s_word;
+    fold_body<R, MAXB, MODE>(smem, s_word, -1, dY, lddy, T, D, P, p_blocks, S, xbuf, x_bytes, sync, accumulate,
+                             nblk, n_tiles, n_split, steps_per, spin_limit, timeouts);
+}
+
 }  // namespace logra

@@ -48,6 +48,13 @@ struct FoldWait {
 hipError_t launch_fold_bf16_tiles(int R, int64_t T, int64_t D, const uint16_t *dY, int64_t lddy,
                                   const uint16_t *P, int p_blocks, float *S, int accumulate,
                                   void *scratch, const FoldWait &wait, hipStream_t st);
+// The pair-mode fold kernel (two members per tile adding their partials
+// inside the launch) for r = R and tiles of at most max_blocks (5 or 10)
+// blocks, on n_wg workgroups; the arguments are the kernel's.
+hipError_t launch_fold_pair_bf16(int R, int max_blocks, int n_wg, hipStream_t st, const uint16_t *dY,
+                                 int64_t lddy, int T, int D, const uint16_t *P, int p_blocks, float *S,
+                                 float *xbuf, int x_bytes, int *sync, int accumulate, int nblk, int n_tiles,
+                                 int n_split, int steps_per, int spin_limit, int *timeouts);
 // Split-mode fold (the sketch of a step held as S plus n_split - 1 parts of
 // d x r fp32): phase bit 0 starts the step (S and the parts overwritten),
 // bit 1 ends it (the parts added into S afterwards, in part order).
