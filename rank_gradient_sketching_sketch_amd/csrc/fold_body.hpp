@@ -417,8 +417,32 @@ __device__ __forceinline__ void fold_body(
 
     // 3. finalize the own rows, in passes of up to kStage rows (a single pass
     // whenever n_split > 1): add the other members' partials, stage, then
-    // read-modify-write S.
-    for (int r0 = own0; r0 < own1; r0 += kStage) {
+    // read-modify-write S. Without an exchange and with at most two passes,
+    // the old values of both passes are requested before the first is
+    // staged, so the second pass does not wait for its loads (with the short
+    // staging tile of the backward kernel's fold, five passes, they would
+    // not fit in its registers).
+    constexpr int kPasses = (16 * MAXB + kStage - 1) / kStage;
+    constexpr bool kEarlyOld = MODE != kFoldPair && kPasses <= 2;
+    u32x4_t old_all[kEarlyOld ? kPasses : 1][kOutChunks];
+    if (kEarlyOld) {
+#pragma unroll
+        for (int q = 0; q < kPasses; ++q) {
+            const int q0 = own0 + q * kStage, q1 = min(q0 + kStage, own1);
+#pragma unroll
+            for (int c = 0; c < kOutChunks; ++c)
+                old_all[q][c] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                 s_rs, accumulate && q0 < own1 ? c_off(q0, q1, c) : kOob, 0, 0));
+        }
+    }
+    // (unrolled where the old values were requested early, so that the index
+    // into them is a constant)
+    constexpr int kUnroll = kEarlyOld ? kPasses : 1;
+#pragma unroll(kUnroll)
+    for (int q = 0; q < kPasses; ++q) {
+        const int r0 = own0 + q * kStage;
+        if (r0 >= own1) break;
         const int r1 = min(r0 + kStage, own1);
         bool timed_out = false;
         if (MODE == kFoldPair) {
@@ -459,10 +483,10 @@ __device__ __forceinline__ void fold_body(
             u32x4_t old[kOutChunks];
 #pragma unroll
             for (int c = 0; c < kOutChunks; ++c)
-                old[c] = MODE == kFoldPair
-                             ? old_pre[c]
-                             : __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
+                old[c] = MODE == kFoldPair ? old_pre[c]
+                         : kEarlyOld       ? old_all[kEarlyOld ? q : 0][c]
+                                           : __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                             s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
 #pragma unroll
             for (int c = 0; c < kOutChunks; ++c) {
                 f32x4_t v = value(c);
