@@ -439,7 +439,7 @@ __device__ __forceinline__ void fold_body(
     // (unrolled where the old values were requested early, so that the index
     // into them is a constant)
     constexpr int kUnroll = kEarlyOld ? kPasses : 1;
-#pragma unroll(kUnroll)
+#pragma unroll kUnroll
     for (int q = 0; q < kPasses; ++q) {
         const int r0 = own0 + q * kStage;
         if (r0 >= own1) break;
