@@ -292,3 +292,21 @@ def test_fold_parts_sizes_and_validation(lib):
     assert lib.logra_sketch_fold_parts(r(m), T, 1, FAKE, 64, FAKE, FAKE, need, 0, FAKE, ws, None, None) == 1
     # T == 0 in a middle microbatch launches nothing and needs no parts
     assert lib.logra_sketch_fold_parts(r(m), 0, 1, None, 0, FAKE, None, 0, 0, None, 0, None, None) == 0
+
+
+def test_per_file_build_flags_name_sources_that_exist():
+    # the fold's register form is set per translation unit; a renamed source
+    # would silently lose its flags
+    from rank_gradient_sketching_sketch_amd import build_lib
+    for name, flags in build_lib.FILE_FLAGS.items():
+        assert os.path.exists(os.path.join(build_lib.CSRC, name)), name
+        assert flags and all(isinstance(f, str) for f in flags)
+
+
+def test_pair_mode_fold_instances_live_only_in_their_own_source():
+    # the pair-mode fold kernels are built without the fold file's register
+    # flag, so no other source may instantiate them
+    csrc = os.path.join(ROOT, "rank_gradient_sketching_sketch_amd", "csrc")
+    users = [f for f in os.listdir(csrc) if f.endswith(".hip")
+             and re.search(r"fold_bf16_kernel<[^>]*kFoldPair>", open(os.path.join(csrc, f)).read())]
+    assert users == ["fold_pair_bf16.hip"]
