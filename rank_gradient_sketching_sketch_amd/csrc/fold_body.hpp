@@ -440,8 +440,8 @@ __device__ __forceinline__ void fold_body(
     // into them is a constant)
     constexpr int kUnroll = kEarlyOld ? kPasses : 1;
 #pragma unroll kUnroll
-    for (int q = 0; q < kPasses; ++q) {
-        const int r0 = own0 + q * kStage;
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int r0 = own0 + pass * kStage;
         if (r0 >= own1) break;
         const int r1 = min(r0 + kStage, own1);
         bool timed_out = false;
@@ -484,7 +484,7 @@ __device__ __forceinline__ void fold_body(
 #pragma unroll
             for (int c = 0; c < kOutChunks; ++c)
                 old[c] = MODE == kFoldPair ? old_pre[c]
-                         : kEarlyOld       ? old_all[kEarlyOld ? q : 0][c]
+                         : kEarlyOld       ? old_all[kEarlyOld ? pass : 0][c]
                                            : __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                                              s_rs, add_old ? c_off(r0, r1, c) : kOob, 0, 0));
 #pragma unroll
